@@ -1,0 +1,59 @@
+"""CPU oracle for Residual Fallback Quantization (RFQ) on MXFP4.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or
+links anything in this package. Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark use it. It shares no code, table or helper
+with the HIP library: it is an independent, slow, float64 statement of what
+the method computes, written so that a reader can check it against the
+sources by eye.
+
+Sources followed (cited by page title and section):
+
+* "Activation Outliers Matter: Robust Recovery for Quantized Multimodal LLMs"
+  (arXiv 2608.26581; Chinese translation page and English summary page),
+  Abstract and §1 (the RFQ paragraph and the contributions list): the
+  activation is split into a primary low-bit (MXFP4) part and the full
+  quantization error, which is itself quantized by a second low-bit path; the
+  residual is re-quantized during the GEMM and its contribution accumulated.
+* The MXFP4 element and scale encodings are only named on those pages (their
+  §3.1 text is cut off). The oracle uses the public OCP Microscaling Formats
+  (MX) v1.0 definitions: 32-element blocks, an E8M0 power-of-two shared scale
+  chosen as floor(log2(amax)) - emax(E2M1), and E2M1 elements (sign, 2-bit
+  exponent with bias 1, 1-bit mantissa) rounded to nearest, ties to even,
+  saturating at +-6.
+
+Every function is pinned by tests in ``tests/test_oracle_*.py`` against facts
+that do not come from this code (worked examples, closed forms, brute force,
+library routines, invariants). The one result without such a pin is the
+model-level accuracy benefit of RFQ, which is outside this package.
+"""
+
+from .formats import (
+    BLOCK,
+    E2M1_EMAX,
+    E2M1_MAGNITUDES,
+    E8M0_NAN,
+    bf16_bits_to_f64,
+    e2m1_value,
+    e8m0_value,
+    f32_bits_to_f64,
+)
+from .quantize import (
+    dequantize,
+    pack_codes,
+    quantize_mxfp4,
+    residual_quantize,
+    scale_exponent,
+    encode_block_elements,
+    unpack_codes,
+)
+from .gemm import gemm_w4a4, linear
+
+__all__ = [
+    "BLOCK", "E2M1_EMAX", "E2M1_MAGNITUDES", "E8M0_NAN",
+    "bf16_bits_to_f64", "f32_bits_to_f64",
+    "e2m1_value", "e8m0_value",
+    "scale_exponent", "encode_block_elements", "quantize_mxfp4", "residual_quantize",
+    "dequantize", "pack_codes", "unpack_codes",
+    "gemm_w4a4", "linear",
+]
