@@ -1,0 +1,162 @@
+/*
+ * rfq.h - C ABI of librfq: Residual Fallback Quantization (RFQ) W4A4 linear
+ * layer on AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Activation Outliers Matter: Robust Recovery for Quantized
+ * Multimodal LLMs", arXiv 2608.26581, Abstract and §1): an activation X is
+ * quantized to MXFP4; the full quantization error R = X - deq(Q(X)) is
+ * quantized to MXFP4 by a second low-bit path; during the GEMM the
+ * residual's product with the FP4 weight is accumulated with the primary
+ * product:  Y = Q(X) Wq^T + Q(R) Wq^T, both in one fp32 accumulator.
+ *
+ * Number formats (named on those pages, defined in the OCP Microscaling
+ * Formats v1.0 specification, which this library follows):
+ *   - a block is 32 consecutive elements of a row along K;
+ *   - shared scale: E8M0 code c, value 2^(c-127); c = 255 is NaN;
+ *     exponent se = max(floor(log2(amax)) - 2, -127), amax = max |x| of the
+ *     block (amax == 0 gives se = -127);
+ *   - element: E2M1 code, bit 3 sign, magnitudes {0,.5,1,1.5,2,3,4,6};
+ *     x / 2^se is rounded to nearest, ties to even, saturating at +-6; the
+ *     sign bit of x is kept (so -0.0 and negatives rounding to zero give 8);
+ *   - a block containing NaN or +-Inf gets scale 255 and element codes 0,
+ *     and so does its residual block.
+ *
+ * Data layout (all row-major, all DEVICE memory unless stated):
+ *   - X: [rows, K] bfloat16, row stride ldx elements (ldx >= K);
+ *   - codes: [rows, K/2] bytes, dense; byte j of a row holds element 2j in
+ *     its low nibble and element 2j+1 in its high nibble;
+ *   - scales: [rows, K/32] bytes, dense, one E8M0 code per block;
+ *   - the weight W [N, K] is quantized along K with rfq_quantize_mxfp4
+ *     (codes [N, K/2], scales [N, K/32]);
+ *   - Y: [M, N] float32 or bfloat16 (rounded to nearest even), row stride
+ *     ldy elements (ldy >= N).
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller owns and allocates every buffer; the library
+ *     allocates no device or pinned memory and keeps no state between calls
+ *     besides a thread-local error string.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) on the current HIP device; buffers must stay alive until
+ *     the stream has run it. Calls are thread-safe.
+ *   - Errors: arguments are checked on the host before anything is enqueued;
+ *     on a non-OK status nothing was launched and no output was written.
+ *     rfq_last_error_detail() then names the failing argument. A failed launch
+ *     returns RFQ_ERR_HIP with the HIP error text in the detail string.
+ *   - Shapes: rows/M, N may be 0 (then nothing is done and RFQ_OK returned);
+ *     K must be positive, a multiple of 32 and at most 2^22; rows, M and N
+ *     below 2^31; rows * K, M * K and N * K below 2^37.
+ *   - Alignment: X and every code pointer 16-byte aligned, and ldx a
+ *     multiple of 8 elements (so every X row starts 16-byte aligned); Y
+ *     aligned to its element size; scale pointers need no alignment; the
+ *     workspace 256-byte aligned.
+ */
+#ifndef RFQ_H_
+#define RFQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RFQ_ABI_VERSION 1
+
+typedef enum rfq_status {
+  RFQ_OK = 0,
+  RFQ_ERR_NULL_POINTER = 1,        /* a required pointer is NULL            */
+  RFQ_ERR_INVALID_SHAPE = 2,       /* negative dim, K <= 0, K % 32, too big */
+  RFQ_ERR_INVALID_STRIDE = 3,      /* ldx < K, ldx % 8 != 0, ldy < N        */
+  RFQ_ERR_MISALIGNED = 4,          /* pointer alignment (see above)         */
+  RFQ_ERR_UNSUPPORTED_DTYPE = 5,   /* dtype code not accepted by this call  */
+  RFQ_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the size needed */
+  RFQ_ERR_HIP = 7                  /* HIP launch or runtime failure         */
+} rfq_status_t;
+
+typedef enum rfq_dtype {
+  RFQ_DTYPE_BF16 = 0,
+  RFQ_DTYPE_FP32 = 1
+} rfq_dtype_t;
+
+/* A hipStream_t passed as an opaque pointer; NULL means the null stream. */
+typedef void* rfq_stream_t;
+
+/*
+ * rfq_quantize_mxfp4 - MXFP4 quantization of a bf16 matrix along K.
+ * (The primary low-bit path of the pages' §1; also quantizes the weight.)
+ *   x       [rows, K] bf16, stride ldx elements.       (in, device)
+ *   codes   [rows, K/2] bytes, dense.                  (out, device)
+ *   scales  [rows, K/32] bytes, dense.                 (out, device)
+ *   x_dtype must be RFQ_DTYPE_BF16.
+ */
+rfq_status_t rfq_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
+                                uint8_t* codes, uint8_t* scales, rfq_stream_t stream);
+
+/*
+ * rfq_residual_quantize - RFQ activation encoding in one pass over X:
+ * Q(X), then R = X - deq(Q(X)) exactly in fp32 (never rounded), then Q(R).
+ * (The pages' §1: the full quantization error, with no threshold, rebuilt by a
+ * second low-bit quantization path.)
+ *   x        [M, K] bf16, stride ldx.                  (in, device)
+ *   qx_codes [M, K/2], qx_scales [M, K/32]: Q(X).      (out, device)
+ *   qr_codes [M, K/2], qr_scales [M, K/32]: Q(R).      (out, device)
+ *   x_dtype must be RFQ_DTYPE_BF16.
+ */
+rfq_status_t rfq_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* qx_codes, uint8_t* qx_scales,
+                                   uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream);
+
+/*
+ * rfq_gemm_w4a4 - block-scaled FP4 GEMM, K-doubled for RFQ:
+ *   Y[m, n] = sum_k deq(QX)[m,k] deq(W)[n,k] + deq(QR)[m,k] deq(W)[n,k]
+ * accumulated in one fp32 accumulator per output (the pages' §1
+ * contributions: the residual is multiplied during the GEMM and its
+ * contribution accumulated). With qr_codes == qr_scales == NULL the residual
+ * term is skipped: plain W4A4.
+ *   qx_codes/qx_scales [M, K/2]/[M, K/32], qr_* likewise (or both NULL),
+ *   w_codes/w_scales [N, K/2]/[N, K/32]                 (in, device)
+ *   y [M, N], y_dtype RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16, stride ldy (out, device)
+ * Scales of 255 (NaN) give NaN outputs; every other input gives finite
+ * outputs except on fp32 overflow.
+ */
+rfq_status_t rfq_gemm_w4a4(const uint8_t* qx_codes, const uint8_t* qx_scales,
+                           const uint8_t* qr_codes, const uint8_t* qr_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales,
+                           int64_t M, int64_t N, int64_t K,
+                           void* y, int y_dtype, int64_t ldy, rfq_stream_t stream);
+
+/* Bytes of workspace rfq_linear needs for an [M, K] activation: Q(X) and
+ * Q(R) codes and scales, each region rounded up to 256 bytes. Host only;
+ * returns 0 for invalid shapes. */
+size_t rfq_linear_workspace_size(int64_t M, int64_t K);
+
+/*
+ * rfq_linear - the whole RFQ W4A4 linear layer: rfq_residual_quantize into
+ * the workspace, then rfq_gemm_w4a4, both on `stream`.
+ *   x [M, K] bf16 stride ldx; w_codes/w_scales: W quantized by
+ *   rfq_quantize_mxfp4; y [M, N] fp32 or bf16 stride ldy;
+ *   workspace: at least rfq_linear_workspace_size(M, K) bytes of device
+ *   memory, 256-byte aligned, owned by the caller; its contents on return
+ *   are Q(X) codes | Q(X) scales | Q(R) codes | Q(R) scales at the offsets
+ *   given by the size rule above.
+ */
+rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                        void* y, int y_dtype, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, rfq_stream_t stream);
+
+/* Static English text for a status code. Host only. */
+const char* rfq_status_string(rfq_status_t status);
+
+/* Thread-local text describing the last non-OK status returned on this
+ * thread ("" if none). Host only; valid until the next call on the thread. */
+const char* rfq_last_error_detail(void);
+
+/* RFQ_ABI_VERSION of the built library. */
+int rfq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RFQ_H_ */

@@ -1,0 +1,110 @@
+"""RFQ W4A4 linear layer for MI355X: Python binding of librfq.
+
+Residual Fallback Quantization ("Activation Outliers Matter: Robust
+Recovery for Quantized Multimodal LLMs", §1): X is quantized to MXFP4, the
+full error R = X - deq(Q(X)) is quantized to MXFP4 again, and
+Y = Q(X) Wq^T + Q(R) Wq^T is one K-doubled block-scaled FP4 GEMM.
+
+This module only marshals torch tensors (device memory and the current HIP
+stream) into the C ABI of include/rfq.h; every step runs in the HIP kernels of
+librfq.so. Nothing falls back to CPU or PyTorch compute: if the library is
+missing, the calls raise.
+"""
+import ctypes
+
+import torch
+
+from ._lib import DTYPE_BF16, DTYPE_FP32, RfqError, check, load
+
+__all__ = [
+    "RfqError",
+    "quantize_mxfp4",
+    "residual_quantize",
+    "gemm_w4a4",
+    "linear",
+    "linear_workspace_size",
+    "library",
+]
+
+
+def library():
+    """The loaded ctypes library (raises if librfq.so is not built)."""
+    return load()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _x_args(x):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along K")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def _y_dtype(out_dtype):
+    if out_dtype == torch.float32:
+        return DTYPE_FP32
+    if out_dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def quantize_mxfp4(x):
+    """MXFP4 along K: returns (codes uint8 [rows, K/2], scales uint8 [rows, K/32])."""
+    rows, K, ldx = _x_args(x)
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    check(load().rfq_quantize_mxfp4(_ptr(x), DTYPE_BF16, rows, K, ldx, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def residual_quantize(x):
+    """RFQ encoding of X: returns (qx, sx, qr, sr) = Q(X) codes/scales, Q(R) codes/scales."""
+    M, K, ldx = _x_args(x)
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    qr = torch.empty_like(qx)
+    sx = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    sr = torch.empty_like(sx)
+    check(load().rfq_residual_quantize(_ptr(x), DTYPE_BF16, M, K, ldx, _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr),
+                                       _stream()))
+    return qx, sx, qr, sr
+
+
+def gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.bfloat16, out=None):
+    """Y = deq(QX) deq(W)^T + deq(QR) deq(W)^T (qr = sr = None: plain W4A4)."""
+    M, N, K = qx.shape[0], wq.shape[0], qx.shape[1] * 2
+    for t in (qx, sx, qr, sr, wq, sw):
+        if t is not None and (t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
+    if wq.shape[1] * 2 != K:
+        raise ValueError("QX and W disagree on K")
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qx.device)
+    if y.stride(1) != 1:
+        raise ValueError("out must have unit stride along N")
+    check(load().rfq_gemm_w4a4(_ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), _ptr(wq), _ptr(sw), M, N, K, _ptr(y),
+                               _y_dtype(y.dtype), y.stride(0), _stream()))
+    return y
+
+
+def linear_workspace_size(M, K):
+    return int(load().rfq_linear_workspace_size(M, K))
+
+
+def linear(x, wq, sw, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """Whole RFQ W4A4 linear layer on bf16 X [M, K] and an MXFP4 weight."""
+    M, K, ldx = _x_args(x)
+    N = wq.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    need = linear_workspace_size(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    check(load().rfq_linear(_ptr(x), DTYPE_BF16, M, K, ldx, _ptr(wq), _ptr(sw), N, _ptr(y), _y_dtype(y.dtype),
+                            y.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    return y

@@ -1,0 +1,188 @@
+// C ABI of librfq (declared in include/rfq.h): argument validation on the
+// host, then stream-ordered launches of the HIP kernels. Nothing here
+// allocates memory; every check runs before anything is enqueued.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kernels.h"
+#include "rfq.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+constexpr int64_t kMaxK = int64_t(1) << 22;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxElems = int64_t(1) << 37;
+
+rfq_status_t fail(rfq_status_t st, const char* fmt, ...) {
+  char buf[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return st;
+}
+
+rfq_status_t ok() {
+  g_detail.clear();
+  return RFQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape rule shared by every entry point: rows in [0, 2^31), K in (0, 2^22]
+// and a multiple of 32, rows * K < 2^37.
+rfq_status_t check_rows_k(int64_t rows, int64_t K, const char* rname) {
+  if (rows < 0 || rows > kMaxRows) return fail(RFQ_ERR_INVALID_SHAPE, "%s = %lld out of range [0, 2^31)", rname, (long long)rows);
+  if (K <= 0 || K % 32 != 0 || K > kMaxK)
+    return fail(RFQ_ERR_INVALID_SHAPE, "K = %lld must be positive, a multiple of 32 and at most 2^22", (long long)K);
+  if (rows * K >= kMaxElems) return fail(RFQ_ERR_INVALID_SHAPE, "%s * K = %lld exceeds 2^37", rname, (long long)(rows * K));
+  return RFQ_OK;
+}
+
+rfq_status_t check_x(const void* x, int x_dtype, int64_t K, int64_t ldx) {
+  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
+  if (ldx < K || ldx % 8 != 0)
+    return fail(RFQ_ERR_INVALID_STRIDE, "ldx = %lld must be >= K = %lld and a multiple of 8", (long long)ldx, (long long)K);
+  if (x == nullptr) return fail(RFQ_ERR_NULL_POINTER, "x is NULL");
+  if (!aligned(x, 16)) return fail(RFQ_ERR_MISALIGNED, "x must be 16-byte aligned");
+  return RFQ_OK;
+}
+
+rfq_status_t check_codes(const void* codes, const void* scales, const char* name) {
+  if (codes == nullptr || scales == nullptr) return fail(RFQ_ERR_NULL_POINTER, "%s codes/scales pointer is NULL", name);
+  if (!aligned(codes, 16)) return fail(RFQ_ERR_MISALIGNED, "%s codes must be 16-byte aligned", name);
+  return RFQ_OK;
+}
+
+rfq_status_t check_y(const void* y, int y_dtype, int64_t N, int64_t ldy) {
+  if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
+  if (ldy < N) return fail(RFQ_ERR_INVALID_STRIDE, "ldy = %lld must be >= N = %lld", (long long)ldy, (long long)N);
+  if (y == nullptr) return fail(RFQ_ERR_NULL_POINTER, "y is NULL");
+  if (!aligned(y, y_dtype == RFQ_DTYPE_FP32 ? 4 : 2)) return fail(RFQ_ERR_MISALIGNED, "y must be aligned to its element size");
+  return RFQ_OK;
+}
+
+rfq_status_t launched(hipError_t e) {
+  if (e != hipSuccess) return fail(RFQ_ERR_HIP, "HIP: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+#define RFQ_TRY(expr)                     \
+  do {                                    \
+    rfq_status_t st_ = (expr);            \
+    if (st_ != RFQ_OK) return st_;        \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+rfq_status_t rfq_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
+                                uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(rows, K, "rows"));
+  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
+  if (rows == 0) return ok();
+  RFQ_TRY(check_x(x, x_dtype, K, ldx));
+  RFQ_TRY(check_codes(codes, scales, "output"));
+  return launched(rfq::launch_quantize(static_cast<const uint16_t*>(x), rows, K, ldx, codes, scales, nullptr,
+                                       nullptr, static_cast<hipStream_t>(stream)));
+}
+
+rfq_status_t rfq_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* qx_codes, uint8_t* qx_scales,
+                                   uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
+  if (M == 0) return ok();
+  RFQ_TRY(check_x(x, x_dtype, K, ldx));
+  RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
+  RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
+  return launched(rfq::launch_quantize(static_cast<const uint16_t*>(x), M, K, ldx, qx_codes, qx_scales, qr_codes,
+                                       qr_scales, static_cast<hipStream_t>(stream)));
+}
+
+rfq_status_t rfq_gemm_w4a4(const uint8_t* qx_codes, const uint8_t* qx_scales,
+                           const uint8_t* qr_codes, const uint8_t* qr_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales,
+                           int64_t M, int64_t N, int64_t K,
+                           void* y, int y_dtype, int64_t ldy, rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_rows_k(N, K, "N"));
+  if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
+  if (M == 0 || N == 0) return ok();
+  RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
+  if ((qr_codes == nullptr) != (qr_scales == nullptr))
+    return fail(RFQ_ERR_NULL_POINTER, "Q(R) codes and scales must be both NULL (plain W4A4) or both set");
+  if (qr_codes != nullptr) RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
+  RFQ_TRY(check_codes(w_codes, w_scales, "W"));
+  RFQ_TRY(check_y(y, y_dtype, N, ldy));
+  return launched(rfq::launch_gemm(qx_codes, qx_scales, qr_codes, qr_scales, w_codes, w_scales, M, N, K, y,
+                                   y_dtype == RFQ_DTYPE_BF16, ldy, static_cast<hipStream_t>(stream)));
+}
+
+size_t rfq_linear_workspace_size(int64_t M, int64_t K) {
+  if (M < 0 || M > kMaxRows || K <= 0 || K % 32 != 0 || K > kMaxK || M * K >= kMaxElems) return 0;
+  const size_t codes = round256((size_t)(M * (K / 2))), scales = round256((size_t)(M * (K / 32)));
+  return 2 * (codes + scales);
+}
+
+rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                        const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                        void* y, int y_dtype, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_rows_k(N, K, "N"));
+  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
+  if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
+  if (M == 0 || N == 0) return ok();
+  RFQ_TRY(check_x(x, x_dtype, K, ldx));
+  RFQ_TRY(check_codes(w_codes, w_scales, "W"));
+  RFQ_TRY(check_y(y, y_dtype, N, ldy));
+  if (workspace == nullptr) return fail(RFQ_ERR_NULL_POINTER, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(RFQ_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  const size_t need = rfq_linear_workspace_size(M, K);
+  if (workspace_bytes < need)
+    return fail(RFQ_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes = %zu, need %zu", workspace_bytes, need);
+
+  const size_t codes = round256((size_t)(M * (K / 2))), scales = round256((size_t)(M * (K / 32)));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* qx = ws;
+  uint8_t* sx = qx + codes;
+  uint8_t* qr = sx + scales;
+  uint8_t* sr = qr + codes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = rfq::launch_quantize(static_cast<const uint16_t*>(x), M, K, ldx, qx, sx, qr, sr, s);
+  if (e != hipSuccess) return launched(e);
+  return launched(rfq::launch_gemm(qx, sx, qr, sr, w_codes, w_scales, M, N, K, y, y_dtype == RFQ_DTYPE_BF16, ldy, s));
+}
+
+const char* rfq_status_string(rfq_status_t status) {
+  switch (status) {
+    case RFQ_OK: return "success";
+    case RFQ_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case RFQ_ERR_INVALID_SHAPE: return "invalid shape";
+    case RFQ_ERR_INVALID_STRIDE: return "invalid row stride";
+    case RFQ_ERR_MISALIGNED: return "misaligned pointer";
+    case RFQ_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case RFQ_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RFQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* rfq_last_error_detail(void) { return g_detail.c_str(); }
+
+int rfq_abi_version(void) { return RFQ_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,20 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the HIP
+// kernels. Arguments here are already validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rfq {
+
+// MXFP4 quantization of a bf16 matrix along K, optionally with the RFQ
+// residual pass (qr/sr non-null). rows * (K/32) must be < 2^32.
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
+                           uint8_t* qx, uint8_t* sx, uint8_t* qr, uint8_t* sr,
+                           hipStream_t stream);
+
+// Block-scaled FP4 GEMM, Y = QX.W^T (+ QR.W^T when qr != nullptr).
+hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, const uint8_t* sr,
+                       const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N, int64_t K,
+                       void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
+
+}  // namespace rfq

@@ -1,0 +1,70 @@
+"""Shared helpers for the GPU parity tests: device transfer and the
+comparison rules. Expected values always come from the CPU oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+# Tolerance on each output, relative to its condition scale S = sum |terms|:
+# fp32 accumulation of the K-doubled sum in an order the oracle does not fix.
+REL_TOL = 1e-5
+BF16_HALF_ULP = 2.0 ** -8          # RNE to bfloat16: |error| <= 2^-8 |value|
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits):
+    """uint16 bf16 bits (numpy) -> CUDA bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def host_bf16_as_f64(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16).astype(np.uint32).__lshift__(16).view(np.float32).astype(
+        np.float64)
+
+
+def oracle_mx(x_bits):
+    """Oracle Q(X) for bf16 bits: packed codes and scales."""
+    codes, scales = oracle.quantize_mxfp4(oracle.bf16_bits_to_f64(x_bits))
+    return oracle.pack_codes(codes), scales
+
+
+def oracle_rfq(x_bits):
+    qx, sx, qr, sr = oracle.residual_quantize(oracle.bf16_bits_to_f64(x_bits))
+    return oracle.pack_codes(qx), sx, oracle.pack_codes(qr), sr
+
+
+def assert_bytes_equal(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatching bytes, first at {bad[:5].tolist()}: " \
+                          f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
+def check_y(y_gpu, y_ref, s_ref, out_dtype, what=""):
+    """Per-output check: fp32 |dY| <= 1e-5 S; bf16 adds the RNE half-ulp."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    tol = REL_TOL * s_ref + 2.0 ** -126
+    if out_dtype == torch.bfloat16:
+        tol = tol * (1 + BF16_HALF_ULP) + BF16_HALF_ULP * np.abs(y_ref) + 2.0 ** -133
+    err = np.abs(y_gpu - y_ref)
+    bad = np.argwhere(~(err <= tol))
+    worst = float(np.max(err / np.maximum(s_ref, 1e-300)))
+    assert bad.size == 0, f"{what}: {len(bad)} outputs out of tolerance, first {bad[:3].tolist()}, " \
+                          f"max |dY|/S = {worst:.3e}"
+    return worst

@@ -1,0 +1,113 @@
+"""The C ABI boundary without a GPU: the library loads, exports every entry
+point include/rfq.h declares, and rejects bad arguments on the host with the
+documented status before anything is launched. Only calls that fail
+validation (or are zero-sized no-ops) are made here."""
+import os
+import re
+
+import pytest
+
+from mxfp4_activation_gemm_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "rfq.h")
+FAKE = 0x10000000          # a well-aligned non-null address; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rfq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported_and_bound(lib):
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+    assert lib.rfq_abi_version() == 1
+
+
+def status_name(st):
+    return _lib.STATUS[st]
+
+
+def q(lib, x=FAKE, dt=0, rows=4, K=64, ldx=64, codes=FAKE, scales=FAKE):
+    return status_name(lib.rfq_quantize_mxfp4(x, dt, rows, K, ldx, codes, scales, None))
+
+
+def test_quantize_validation(lib):
+    assert q(lib, x=None) == "RFQ_ERR_NULL_POINTER"
+    assert "x is NULL" in lib.rfq_last_error_detail().decode()
+    assert q(lib, codes=None) == "RFQ_ERR_NULL_POINTER"
+    assert q(lib, K=48, ldx=48) == "RFQ_ERR_INVALID_SHAPE"
+    assert q(lib, K=0, ldx=0) == "RFQ_ERR_INVALID_SHAPE"
+    assert q(lib, K=1 << 23, ldx=1 << 23) == "RFQ_ERR_INVALID_SHAPE"
+    assert q(lib, rows=-1) == "RFQ_ERR_INVALID_SHAPE"
+    assert q(lib, rows=1 << 31) == "RFQ_ERR_INVALID_SHAPE"
+    assert q(lib, rows=1 << 22, K=1 << 15, ldx=1 << 15) == "RFQ_ERR_INVALID_SHAPE"   # 2^37 elements
+    assert q(lib, dt=1) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert q(lib, ldx=32) == "RFQ_ERR_INVALID_STRIDE"
+    assert q(lib, ldx=68) == "RFQ_ERR_INVALID_STRIDE"
+    assert q(lib, x=FAKE + 8) == "RFQ_ERR_MISALIGNED"
+    assert q(lib, codes=FAKE + 4) == "RFQ_ERR_MISALIGNED"
+    assert q(lib, x=None, rows=0) == "RFQ_OK"              # empty input: no-op, pointers unused
+    assert lib.rfq_last_error_detail().decode() == ""
+
+
+def test_residual_quantize_validation(lib):
+    f = lib.rfq_residual_quantize
+    assert status_name(f(FAKE, 0, 4, 64, 64, FAKE, FAKE, None, FAKE, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(f(FAKE, 0, 4, 64, 64, FAKE, FAKE, FAKE + 1, FAKE, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(f(FAKE, 0, 4, 96, 100, FAKE, FAKE, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_STRIDE"
+    assert status_name(f(None, 0, 0, 64, 64, None, None, None, None, None)) == "RFQ_OK"
+
+
+def g(lib, qx=FAKE, sx=FAKE, qr=FAKE, sr=FAKE, w=FAKE, sw=FAKE, M=8, N=8, K=64, y=FAKE, yd=0, ldy=8):
+    return status_name(lib.rfq_gemm_w4a4(qx, sx, qr, sr, w, sw, M, N, K, y, yd, ldy, None))
+
+
+def test_gemm_validation(lib):
+    assert g(lib, qr=FAKE, sr=None) == "RFQ_ERR_NULL_POINTER"
+    assert g(lib, qr=None, sr=FAKE) == "RFQ_ERR_NULL_POINTER"
+    assert g(lib, w=None) == "RFQ_ERR_NULL_POINTER"
+    assert g(lib, y=None) == "RFQ_ERR_NULL_POINTER"
+    assert g(lib, K=40) == "RFQ_ERR_INVALID_SHAPE"
+    assert g(lib, N=-3) == "RFQ_ERR_INVALID_SHAPE"
+    assert g(lib, yd=7) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert g(lib, ldy=4) == "RFQ_ERR_INVALID_STRIDE"
+    assert g(lib, y=FAKE + 1, yd=0) == "RFQ_ERR_MISALIGNED"
+    assert g(lib, y=FAKE + 2, yd=1) == "RFQ_ERR_MISALIGNED"
+    assert g(lib, w=FAKE + 8) == "RFQ_ERR_MISALIGNED"
+    assert g(lib, M=0, qx=None, y=None) == "RFQ_OK"
+    assert g(lib, N=0, w=None, y=None) == "RFQ_OK"
+
+
+def test_linear_workspace_rule_and_validation(lib):
+    ws = lib.rfq_linear_workspace_size
+    r256 = lambda b: (b + 255) // 256 * 256
+    for M, K in [(1, 32), (64, 256), (4096, 5120), (32768, 13824), (3, 96)]:
+        assert ws(M, K) == 2 * (r256(M * K // 2) + r256(M * K // 32))
+    assert ws(4, 48) == 0 and ws(-1, 64) == 0 and ws(0, 64) == 0
+    f = lib.rfq_linear
+    need = ws(8, 64)
+    assert status_name(f(FAKE, 0, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, FAKE, need - 1, None)) == \
+        "RFQ_ERR_WORKSPACE_TOO_SMALL"
+    assert status_name(f(FAKE, 0, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, None, need, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(f(FAKE, 0, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, FAKE + 16, need, None)) == \
+        "RFQ_ERR_MISALIGNED"
+    assert status_name(f(FAKE, 1, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, FAKE, need, None)) == \
+        "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert status_name(f(None, 0, 0, 64, 64, None, None, 8, None, 0, 8, None, 0, None)) == "RFQ_OK"
+
+
+def test_status_strings(lib):
+    assert lib.rfq_status_string(0) == b"success"
+    for code in range(1, 8):
+        assert lib.rfq_status_string(code) not in (b"", b"unknown status")
+    assert lib.rfq_status_string(99) == b"unknown status"

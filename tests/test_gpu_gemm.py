@@ -1,0 +1,221 @@
+"""GPU parity of the W4A4 GEMM and the whole RFQ linear layer against the
+oracle: codes and scales bit-exact, Y within 1e-5 of the condition scale
+per output (plus the bf16 rounding half-ulp for bf16 outputs)."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_activation_gemm_amd as rfq
+import oracle
+import workloads
+from gpu_helpers import (assert_bytes_equal, check_y, dev_bf16, dev_u8, host, host_bf16_as_f64, log, oracle_mx,
+                         oracle_rfq)
+
+pytestmark = pytest.mark.gpu
+
+SPEC_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rfq.library()
+
+
+def y_host(y):
+    return host_bf16_as_f64(y) if y.dtype == torch.bfloat16 else host(y).astype(np.float64)
+
+
+def oracle_y(x_bits, w_bits, resid=True):
+    x = oracle.bf16_bits_to_f64(x_bits)
+    w = oracle.bf16_bits_to_f64(w_bits)
+    wq, sw = oracle.quantize_mxfp4(w)
+    qx, sx, qr, sr = oracle.residual_quantize(x)
+    if not resid:
+        qr = sr = None
+    return oracle.gemm_w4a4(qx, sx, qr, sr, wq, sw)
+
+
+def heavy(rng, rows, K, outliers=3):
+    x = rng.standard_t(3, size=(rows, K)).astype(np.float32)
+    if outliers:
+        x[:, rng.choice(K, size=min(outliers, K), replace=False)] *= 60
+    return workloads.f32_to_bf16_bits(x)
+
+
+def test_tiny_config_every_output_fp32():
+    cfg = workloads.CONFIGS["tiny"]
+    xb, wb = workloads.x_bf16(cfg), workloads.w_bf16(cfg)
+    log("[gemm] tiny config")
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    y = rfq.linear(dev_bf16(xb), wq, sw, out_dtype=torch.float32)
+    y_ref, s_ref = oracle_y(xb, wb)
+    worst = check_y(y_host(y), y_ref, s_ref, torch.float32, "tiny")
+    log(f"   max |dY|/S = {worst:.2e}")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 416), (1, 1, 32), (33, 65, 96), (257, 255, 128), (70, 300, 4128),
+                                   (512, 512, 1024)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_ragged_shapes_every_output(M, N, K, out_dtype):
+    rng = np.random.default_rng(M * 7 + N * 13 + K)
+    xb, wb = heavy(rng, M, K), workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[gemm] ragged M={M} N={N} K={K} {out_dtype}")
+    x = dev_bf16(xb)
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    y = rfq.linear(x, wq, sw, out_dtype=out_dtype)
+    y_ref, s_ref = oracle_y(xb, wb)
+    check_y(y_host(y), y_ref, s_ref, out_dtype, f"rfq {M}x{N}x{K}")
+    # plain W4A4 through the same kernel family
+    qx, sx, _, _ = rfq.residual_quantize(x)
+    y1 = rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out_dtype=out_dtype)
+    y1_ref, s1_ref = oracle_y(xb, wb, resid=False)
+    check_y(y_host(y1), y1_ref, s1_ref, out_dtype, f"w4a4 {M}x{N}x{K}")
+
+
+def test_all_code_pairs_single_block():
+    # row a of Q(X) holds code a at k = 7, row b of W holds code b there; unit
+    # scales: Y[a, b] = value(a) * value(b) exactly
+    qx = np.zeros((16, 32), np.uint8)
+    wq = np.zeros((16, 32), np.uint8)
+    qx[:, 7] = np.arange(16)
+    wq[:, 7] = np.arange(16)
+    ones = np.full((16, 1), 127, np.uint8)
+    log("[gemm] code pairs")
+    y = rfq.gemm_w4a4(dev_u8(oracle.pack_codes(qx)), dev_u8(ones), None, None, dev_u8(oracle.pack_codes(wq)),
+                      dev_u8(ones), out_dtype=torch.float32)
+    vals = np.array(SPEC_E2M1 + [-v for v in SPEC_E2M1])
+    assert (host(y) == np.outer(vals, vals)).all()
+
+
+def test_every_code_in_every_lane_position():
+    # random codes at every (row, k) with scale codes spread over a wide range
+    rng = np.random.default_rng(21)
+    M, N, K = 96, 160, 640
+    qx = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    qr = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    wq = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    sx = rng.integers(64, 170, (M, K // 32)).astype(np.uint8)
+    sr = rng.integers(64, 170, (M, K // 32)).astype(np.uint8)
+    sw = rng.integers(64, 170, (N, K // 32)).astype(np.uint8)
+    log("[gemm] random codes and scales")
+    y = rfq.gemm_w4a4(dev_u8(oracle.pack_codes(qx)), dev_u8(sx), dev_u8(oracle.pack_codes(qr)), dev_u8(sr),
+                      dev_u8(oracle.pack_codes(wq)), dev_u8(sw), out_dtype=torch.float32)
+    y_ref, s_ref = oracle.gemm_w4a4(qx, sx, qr, sr, wq, sw)
+    check_y(host(y), y_ref, s_ref, torch.float32, "random codes")
+
+
+def test_selector_weight_returns_dequantized_activations():
+    cfg = workloads.CONFIGS["tiny"]
+    xb = workloads.x_bf16(cfg)
+    K = cfg.K
+    w = np.eye(K, dtype=np.float32)[:128]
+    wb = workloads.f32_to_bf16_bits(w)
+    log("[gemm] selector")
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    y = rfq.linear(dev_bf16(xb), wq, sw, out_dtype=torch.float32)
+    qx, sx, qr, sr = oracle.residual_quantize(oracle.bf16_bits_to_f64(xb))
+    want = (oracle.dequantize(qx, sx) + oracle.dequantize(qr, sr))[:, :128]
+    assert (host(y).astype(np.float64) == want).all()
+
+
+def test_nan_block_gives_nan_outputs_only_in_its_row():
+    rng = np.random.default_rng(22)
+    M, N, K = 64, 96, 256
+    xb = heavy(rng, M, K)
+    xb[5, 40] = 0x7FC0          # NaN
+    xb[9, 200] = 0x7F80         # +Inf
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log("[gemm] NaN/Inf blocks")
+    x = dev_bf16(xb)
+    qx, sx, qr, sr = rfq.residual_quantize(x)
+    oqx, osx, oqr, osr = oracle_rfq(xb)
+    assert_bytes_equal(host(sx), osx, "SX")
+    assert_bytes_equal(host(sr), osr, "SR")
+    assert_bytes_equal(host(qx), oqx, "QX")
+    assert_bytes_equal(host(qr), oqr, "QR")
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    y = host(rfq.gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.float32))
+    assert np.isnan(y[5]).all() and np.isnan(y[9]).all()
+    ok_rows = [r for r in range(M) if r not in (5, 9)]
+    assert np.isfinite(y[ok_rows]).all()
+
+
+def test_linear_equals_quantize_then_gemm_bitwise_and_is_deterministic():
+    rng = np.random.default_rng(23)
+    M, N, K = 384, 640, 2048
+    xb = heavy(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    x = dev_bf16(xb)
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    log("[gemm] linear vs two calls")
+    ws = torch.empty(rfq.linear_workspace_size(M, K), dtype=torch.uint8, device="cuda")
+    y1 = rfq.linear(x, wq, sw, out_dtype=torch.float32, workspace=ws)
+    qx, sx, qr, sr = rfq.residual_quantize(x)
+    y2 = rfq.gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.float32)
+    y3 = rfq.linear(x, wq, sw, out_dtype=torch.float32)
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    # the workspace holds Q(X) | SX | Q(R) | SR at 256-byte-rounded offsets
+    r256 = lambda b: (b + 255) // 256 * 256
+    c, s = r256(M * K // 2), r256(M * K // 32)
+    wsh = host(ws)
+    assert (wsh[:M * K // 2] == host(qx).ravel()).all()
+    assert (wsh[c:c + M * K // 32] == host(sx).ravel()).all()
+    assert (wsh[c + s:c + s + M * K // 2] == host(qr).ravel()).all()
+    assert (wsh[2 * c + s:2 * c + s + M * K // 32] == host(sr).ravel()).all()
+
+
+def test_output_row_stride():
+    rng = np.random.default_rng(24)
+    M, N, K = 40, 72, 192
+    xb, wb = heavy(rng, M, K), workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    big = torch.full((M, N + 24), 7.0, dtype=torch.float32, device="cuda")
+    log("[gemm] strided output")
+    rfq.linear(dev_bf16(xb), wq, sw, out=big[:, :N])
+    yh = host(big)
+    assert (yh[:, N:] == 7.0).all()
+    y_ref, s_ref = oracle_y(xb, wb)
+    check_y(yh[:, :N], y_ref, s_ref, torch.float32, "strided out")
+
+
+@pytest.mark.parametrize("name", ["qwen3vl_attn_proj", "qwen3vl_ffn_up", "wan22_ffn", "dit_ffn_down"])
+def test_full_size_config_sampled(name):
+    """The configuration as the benchmark runs it (full X, full W, bf16 Y, one
+    rfq_linear call); the oracle checks a sample of rows of Q(X), Q(R) and of
+    the weight codes bit for bit, and the outputs at sampled rows x sampled
+    columns."""
+    cfg = workloads.CONFIGS[name]
+    log(f"[gemm] full size {name} M={cfg.M} N={cfg.N} K={cfg.K}: generating")
+    xb = workloads.x_bf16(cfg)
+    wb = workloads.w_bf16(cfg)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    log("   running on the GPU")
+    wq, sw = rfq.quantize_mxfp4(w)
+    ws = torch.empty(rfq.linear_workspace_size(cfg.M, cfg.K), dtype=torch.uint8, device="cuda")
+    y = rfq.linear(x, wq, sw, out_dtype=torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(cfg, n_random=126)
+    cols = np.unique(np.concatenate([[0, cfg.N - 1],
+                                     np.random.default_rng(cfg.seed).choice(cfg.N, 254, replace=False)]))
+    M, K = cfg.M, cfg.K
+    r256 = lambda b: (b + 255) // 256 * 256
+    c, s = r256(M * K // 2), r256(M * K // 32)
+    wsh = host(ws)
+    gqx = wsh[:M * K // 2].reshape(M, K // 2)[rows]
+    gsx = wsh[c:c + M * K // 32].reshape(M, K // 32)[rows]
+    gqr = wsh[c + s:c + s + M * K // 2].reshape(M, K // 2)[rows]
+    gsr = wsh[2 * c + s:2 * c + s + M * K // 32].reshape(M, K // 32)[rows]
+    log(f"   oracle on {len(rows)} rows x {len(cols)} columns")
+    oqx, osx, oqr, osr = oracle_rfq(xb[rows])
+    assert_bytes_equal(gqx, oqx, "Q(X) sampled rows")
+    assert_bytes_equal(gsx, osx, "SX sampled rows")
+    assert_bytes_equal(gqr, oqr, "Q(R) sampled rows")
+    assert_bytes_equal(gsr, osr, "SR sampled rows")
+    owq, osw = oracle_mx(wb[cols])
+    assert_bytes_equal(host(wq)[cols], owq, "W codes sampled rows")
+    assert_bytes_equal(host(sw)[cols], osw, "W scales sampled rows")
+    y_ref, s_ref = oracle_y(xb[rows], wb[cols])
+    yh = host_bf16_as_f64(y)[np.ix_(rows, cols)]
+    worst = check_y(yh, y_ref, s_ref, torch.bfloat16, name)
+    log(f"   ok, max |dY|/S = {worst:.2e}")
