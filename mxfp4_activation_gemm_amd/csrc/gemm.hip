@@ -16,14 +16,25 @@
 //
 // Tiling: a 256 x 256 output tile per workgroup of 4 waves (2 x 2), each
 // wave 128 x 128 = 4 x 4 MFMA tiles (256 fp32 accumulators per lane).
-// K advances 128 elements per stage (two MFMA steps). Per stage the QX, QR
-// and W tiles go global -> LDS by buffer loads that write LDS directly,
-// already in MFMA lane order (one 1 KB fragment per load instruction), so
-// every LDS read is a contiguous, conflict-free ds_read_b128. Buffer loads
-// return zero outside the tensor, which covers partial M, N and K tiles.
-// Scales (4 bytes per row per stage) are loaded straight into registers.
-// Two LDS stages; the next stage's loads are issued after this stage's
-// fragments are in registers and overlap its 64 MFMAs.
+// K advances 128 elements (64 bytes of codes per row) per stage, two MFMA
+// steps.
+//
+// Data movement, per stage:
+//  * Code tiles (QX, QR, W; 256 rows x 64 B each) go global -> LDS with
+//    buffer loads that write LDS directly. Four consecutive lanes fetch one
+//    row's 64 contiguous bytes, so each quad touches one cache line. In LDS a
+//    row is 4 chunks of 16 B (one K-block each); chunk c of row r sits at
+//    position c ^ f(r), f(r) = (r >> 2) & 3, which makes the MFMA operand
+//    reads (32 rows, same chunk) free of LDS bank conflicts on gfx950
+//    (measured with the LDS bank-conflict counter; swizzles that are
+//    conflict-free under a plain 32- or 64-bank model were not). The swizzle
+//    is applied by choosing which chunk each lane fetches; the LDS slot of a
+//    lane is fixed by the hardware.
+//  * Scales are fetched 16 B per row (16 blocks = 4 stages) into a separate
+//    LDS area every fourth stage; each stage reads its 4-byte word per row.
+//  * Buffer loads return zero outside the tensor, which covers partial M
+//    and N tiles; partial K is masked per 16-byte chunk.
+// Two LDS stages: stage s + 1 is loaded while stage s's 64 MFMAs run.
 
 #include "kernels.h"
 
@@ -41,12 +52,20 @@ constexpr int kWavesM = 2, kWavesN = 2;
 constexpr int kTM = kBM / kWavesM / 32;     // 4 MFMA tiles along M per wave
 constexpr int kTN = kBN / kWavesN / 32;     // 4 along N
 constexpr int kSteps = kBK / 64;            // 2 MFMA K-steps per stage
-constexpr int kFrag = 1024;                 // 32 rows x 32 bytes
-constexpr int kTileBytesA = kBM / 32 * kSteps * kFrag;   // 16 KB
-constexpr int kTileBytesB = kBN / 32 * kSteps * kFrag;   // 16 KB
+constexpr int kRowBytes = kBK / 2;          // 64 bytes of codes per row per stage
+constexpr int kTileBytesA = kBM * kRowBytes;           // 16 KB
+constexpr int kTileBytesB = kBN * kRowBytes;           // 16 KB
 constexpr int kStageBytes = 2 * kTileBytesA + kTileBytesB;  // X, R, W
+constexpr int kScaleGroup = 4;              // stages per scale fetch (16 blocks)
+constexpr int kScaleRowBytes = 16;
+constexpr int kScaleBytesA = kBM * kScaleRowBytes;     // 4 KB
+constexpr int kScaleBytes = 2 * kScaleBytesA + kBN * kScaleRowBytes;
+constexpr int kLdsBytes = 2 * kStageBytes + 2 * kScaleBytes;   // 120 KB
 constexpr uint32_t kOOB = 0x80000000u;      // voffset that is always out of range
 constexpr int kGroupM = 4;                  // tile rows swept together (L2 reuse)
+constexpr int kLoadsPerTile = kBM / 16 / 4; // 16-row load instructions per wave per tile (4)
+
+static_assert(kBM == kBN, "the load distribution below assumes square tiles");
 
 struct GemmParams {
   const uint8_t* qx;
@@ -61,23 +80,20 @@ struct GemmParams {
   int32_t tiles_m, tiles_n;
 };
 
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 2) & 3u; }
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // gfx9 raw buffer: stride 0, num_records in bytes, dword3 = 32-bit data format
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void load_frag_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
-__device__ __forceinline__ i32x8_t read_frag(const uint8_t* lds_frag, unsigned lane) {
-  const i32x4_t v = *reinterpret_cast<const i32x4_t*>(lds_frag + lane * 16);
+__device__ __forceinline__ i32x8_t read_frag(const uint8_t* p) {
+  const i32x4_t v = *reinterpret_cast<const i32x4_t*>(p);
   return i32x8_t{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-}
-
-// One 32-bit word = the E8M0 scales of 4 consecutive blocks of one row.
-__device__ __forceinline__ uint32_t load_scale_word(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
 }
 
 // Maps a workgroup id to an output tile: first spread consecutive tiles of
@@ -119,9 +135,12 @@ __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x8
   }
 }
 
-template <bool kResid, bool kOutBf16, bool kKAligned>
+// kFast: K % 512 == 0 (whole stages and whole 16-block scale groups).
+template <bool kResid, bool kOutBf16, bool kFast>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  uint8_t* const tiles = lds;
+  uint8_t* const scales = lds + 2 * kStageBytes;
 
   const unsigned lane = threadIdx.x & 63;
   const unsigned wave = threadIdx.x >> 6;
@@ -139,22 +158,78 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rsr = make_rsrc(kResid ? p.sr + (int64_t)m0 * kblocks : p.sx, rows_a * kblocks);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
 
-  // This wave loads fragments (row-frag f, step s) for f in {2 wave, 2 wave + 1}
-  // of each of X, R and W; lane l fetches row 32 f + l % 32, bytes 32 s + 16 (l / 32).
+  // Code-tile loads: this wave fetches tile rows [64 wave, 64 wave + 64) of
+  // each operand, 16 rows per instruction; lane l takes row 16 n + l / 4 and
+  // chunk (l % 4) ^ f(row) of it.
   const unsigned lrow = lane & 31, lhalf = lane >> 5;
-  uint32_t frag_voff[2][kSteps];
+  uint32_t ld_voff[kLoadsPerTile];
+  uint32_t ld_chunk[kLoadsPerTile];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      frag_voff[f][s] = (32 * (2 * wave + f) + lrow) * kbytes + 32 * s + 16 * lhalf;
+  for (int n = 0; n < kLoadsPerTile; ++n) {
+    const uint32_t row = 64 * wave + 16 * n + (lane >> 2);
+    ld_chunk[n] = (lane & 3) ^ swz(row);
+    ld_voff[n] = row * kbytes + 16 * ld_chunk[n];
+  }
 
-  // Scale words: the 4 consecutive block scales (one stage) of this lane's rows.
-  uint32_t sc_voff_a[kTM], sc_voff_b[kTN];
+  auto issue_stage = [&](int st, uint8_t* buf) {
+    const uint32_t kb = (uint32_t)st * kRowBytes;
 #pragma unroll
-  for (int i = 0; i < kTM; ++i) sc_voff_a[i] = (kBM / kWavesM * wm + 32 * i + lrow) * kblocks;
+    for (int n = 0; n < kLoadsPerTile; ++n) {
+      uint32_t vo = ld_voff[n] + kb;
+      if (!kFast && (uint32_t)st * (kBK / 32) + ld_chunk[n] >= kblocks) vo = kOOB;
+      uint8_t* dst = buf + (64 * wave + 16 * n) * kRowBytes;
+      load16_to_lds(rx, dst, vo);
+      if (kResid) load16_to_lds(rr, dst + kTileBytesA, vo);
+      load16_to_lds(rw, dst + 2 * kTileBytesA, vo);
+    }
+  };
+
+  // Scale loads for group g (stages 4g .. 4g + 3): 16 bytes per row, lane l
+  // of instruction j takes row 64 (j % 4) + l of operand j / 4 (X, R, W);
+  // wave w issues j = 3w, 3w + 1, 3w + 2.
+  auto issue_scale_rows = [&](__amdgpu_buffer_rsrc_t r, int g, uint8_t* dst, uint32_t row) {
+      if (kFast) {
+        load16_to_lds(r, dst, row * kblocks + 16 * g);
+      } else {
+        // gather byte by byte; blocks past K get a finite scale (their codes are zero)
+        uint32_t wv[4];
 #pragma unroll
-  for (int j = 0; j < kTN; ++j) sc_voff_b[j] = (kBN / kWavesN * wn + 32 * j + lrow) * kblocks;
+        for (int d = 0; d < 4; ++d) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t blk = 16 * g + 4 * d + e;
+            const uint32_t b = blk < kblocks ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, row * kblocks + blk, 0, 0)
+                                             : 127u;
+            v |= b << (8 * e);
+          }
+          wv[d] = v;
+        }
+        *reinterpret_cast<i32x4_t*>(dst + lane * kScaleRowBytes) =
+            i32x4_t{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+      }
+  };
+  auto issue_scales = [&](int g, uint8_t* sbuf) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int j = 3 * (int)wave + q;   // wave-uniform: plain branches, no descriptor select
+      const uint32_t row = 64 * (j % 4) + lane;
+      uint8_t* dst = sbuf + (j / 4) * kScaleBytesA + 64 * (j % 4) * kScaleRowBytes;
+      if (j < 4)
+        issue_scale_rows(rsx, g, dst, row);
+      else if (j < 8) {
+        if (kResid) issue_scale_rows(rsr, g, dst, row);
+      } else
+        issue_scale_rows(rsw, g, dst, row);
+    }
+  };
+
+  // Per-lane LDS read offsets. A fragment of 32 rows starting at tile row
+  // 32 t: lane (lhalf, lrow) reads chunk (2 s + lhalf) of row 32 t + lrow.
+  uint32_t rd_off[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) rd_off[s] = lrow * kRowBytes + 16 * ((2 * s + lhalf) ^ swz(lrow));
+  const uint32_t a_row0 = kBM / kWavesM * wm, b_row0 = kBN / kWavesN * wn;
 
   f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -165,63 +240,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   const int nstages = (p.K + kBK - 1) / kBK;
-
-  auto issue_stage = [&](int st, uint8_t* buf) {
-    const uint32_t kb = (uint32_t)st * (kBK / 2);        // byte offset of the stage in a row
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        uint32_t vo = frag_voff[f][s] + kb;
-        if (!kKAligned) {
-          const uint32_t blk = (uint32_t)st * (kBK / 32) + 2 * s + lhalf;
-          if (blk >= kblocks) vo = kOOB;
-        }
-        const int frag = (2 * wave + f) * kSteps + s;
-        load_frag_to_lds(rx, buf + frag * kFrag, vo);
-        if (kResid) load_frag_to_lds(rr, buf + kTileBytesA + frag * kFrag, vo);
-        load_frag_to_lds(rw, buf + 2 * kTileBytesA + frag * kFrag, vo);
-      }
-  };
-
-  auto load_scales = [&](int st, uint32_t (&scx)[kTM], uint32_t (&scr)[kTM], uint32_t (&scw)[kTN]) {
-    const uint32_t kb = (uint32_t)st * (kBK / 32);
-    if (kKAligned) {
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        scx[i] = load_scale_word(rsx, sc_voff_a[i] + kb);
-        if (kResid) scr[i] = load_scale_word(rsr, sc_voff_a[i] + kb);
-      }
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) scw[j] = load_scale_word(rsw, sc_voff_b[j] + kb);
-    } else {
-      // K not a multiple of 128: gather the bytes one by one into the same
-      // word layout; blocks past K read as zero codes with a finite scale.
-      auto byte_at = [&](__amdgpu_buffer_rsrc_t r, uint32_t row_off, uint32_t blk) -> uint32_t {
-        if (blk >= kblocks) return 127u;
-        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, row_off + blk, 0, 0);
-      };
-      auto word_at = [&](__amdgpu_buffer_rsrc_t r, uint32_t row_off) -> uint32_t {
-        return byte_at(r, row_off, kb) | (byte_at(r, row_off, kb + 1) << 8) |
-               (byte_at(r, row_off, kb + 2) << 16) | (byte_at(r, row_off, kb + 3) << 24);
-      };
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        scx[i] = word_at(rsx, sc_voff_a[i]);
-        if (kResid) scr[i] = word_at(rsr, sc_voff_a[i]);
-      }
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) scw[j] = word_at(rsw, sc_voff_b[j]);
-    }
-  };
-
-  uint32_t scx[kTM], scr[kTM], scw[kTN];
-  issue_stage(0, lds[0]);
-  load_scales(0, scx, scr, scw);
+  issue_scales(0, scales);
+  issue_stage(0, tiles);
 
   for (int st = 0; st < nstages; ++st) {
-    uint8_t* buf = lds[st & 1];
-    __builtin_amdgcn_s_waitcnt(0);      // this stage's LDS writes and scale words have landed
+    const uint8_t* buf = tiles + (st & 1) * kStageBytes;
+    const uint8_t* sbuf = scales + ((st / kScaleGroup) & 1) * kScaleBytes;
+    __builtin_amdgcn_s_waitcnt(0);      // this stage's tiles and scales have landed in LDS
     __syncthreads();
 
     i32x8_t ax[kSteps][kTM], ar[kSteps][kTM], bw[kSteps][kTN];
@@ -229,32 +254,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
-        const int frag = (kTM * wm + i) * kSteps + s;
-        ax[s][i] = read_frag(buf + frag * kFrag, lane);
-        if (kResid) ar[s][i] = read_frag(buf + kTileBytesA + frag * kFrag, lane);
+        const uint8_t* src = buf + (a_row0 + 32 * i) * kRowBytes + rd_off[s];
+        ax[s][i] = read_frag(src);
+        if (kResid) ar[s][i] = read_frag(src + kTileBytesA);
       }
 #pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        bw[s][j] = read_frag(buf + 2 * kTileBytesA + ((kTN * wn + j) * kSteps + s) * kFrag, lane);
+      for (int j = 0; j < kTN; ++j) bw[s][j] = read_frag(buf + 2 * kTileBytesA + (b_row0 + 32 * j) * kRowBytes + rd_off[s]);
     }
-    // Byte 2s of each shifted word is the scale of block (4 st + 2 s + lhalf).
+    // Scale words of this stage: byte 2 s of (word >> 8 lhalf) is the scale of
+    // block 4 st + 2 s + lhalf of the lane's row.
+    const uint32_t sofs = (st % kScaleGroup) * 4;
     uint32_t cx[kTM], cr[kTM], cw[kTN];
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) { cx[i] = scx[i] >> (8 * lhalf); cr[i] = scr[i] >> (8 * lhalf); }
+    for (int i = 0; i < kTM; ++i) {
+      const uint8_t* s0 = sbuf + (a_row0 + 32 * i + lrow) * kScaleRowBytes + sofs;
+      cx[i] = *reinterpret_cast<const uint32_t*>(s0) >> (8 * lhalf);
+      cr[i] = kResid ? *reinterpret_cast<const uint32_t*>(s0 + kScaleBytesA) >> (8 * lhalf) : 0u;
+    }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) cw[j] = scw[j] >> (8 * lhalf);
+    for (int j = 0; j < kTN; ++j)
+      cw[j] = *reinterpret_cast<const uint32_t*>(sbuf + 2 * kScaleBytesA + (b_row0 + 32 * j + lrow) * kScaleRowBytes +
+                                                 sofs) >> (8 * lhalf);
 
     if (st + 1 < nstages) {
-      issue_stage(st + 1, lds[(st + 1) & 1]);
-      load_scales(st + 1, scx, scr, scw);
+      if ((st + 1) % kScaleGroup == 0) issue_scales((st + 1) / kScaleGroup, scales + (((st + 1) / kScaleGroup) & 1) * kScaleBytes);
+      issue_stage(st + 1, tiles + ((st + 1) & 1) * kStageBytes);
     }
     mfma_step<0, kResid>(acc, ax[0], ar[0], bw[0], cx, cr, cw);
     mfma_step<1, kResid>(acc, ax[1], ar[1], bw[1], cx, cr, cw);
   }
 
   // Epilogue: fp32 accumulators to Y.
-  const int row_base = m0 + kBM / kWavesM * wm + 4 * lhalf;
-  const int col_base = n0 + kBN / kWavesN * wn + lrow;
+  const int row_base = m0 + (int)a_row0 + 4 * (int)lhalf;
+  const int col_base = n0 + (int)b_row0 + (int)lrow;
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -278,8 +310,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 }
 
 template <bool kResid, bool kOutBf16>
-hipError_t launch_variant(const GemmParams& p, bool kaligned, int grid, hipStream_t stream) {
-  if (kaligned)
+hipError_t launch_variant(const GemmParams& p, bool fast, int grid, hipStream_t stream) {
+  if (fast)
     hipLaunchKernelGGL((gemm_kernel<kResid, kOutBf16, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((gemm_kernel<kResid, kOutBf16, false>), dim3(grid), dim3(kThreads), 0, stream, p);
@@ -298,13 +330,13 @@ hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, 
   p.tiles_m = (int32_t)((M + kBM - 1) / kBM);
   p.tiles_n = (int32_t)((N + kBN - 1) / kBN);
   const int grid = p.tiles_m * p.tiles_n;
-  const bool kaligned = (K % kBK) == 0;
+  const bool fast = (K % (kBK * kScaleGroup)) == 0;
   const bool resid = qr != nullptr;
   if (resid)
-    return y_bf16 ? launch_variant<true, true>(p, kaligned, grid, stream)
-                  : launch_variant<true, false>(p, kaligned, grid, stream);
-  return y_bf16 ? launch_variant<false, true>(p, kaligned, grid, stream)
-                : launch_variant<false, false>(p, kaligned, grid, stream);
+    return y_bf16 ? launch_variant<true, true>(p, fast, grid, stream)
+                  : launch_variant<true, false>(p, fast, grid, stream);
+  return y_bf16 ? launch_variant<false, true>(p, fast, grid, stream)
+                : launch_variant<false, false>(p, fast, grid, stream);
 }
 
 }  // namespace rfq
