@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the RFQ W4A4 linear layer on one MI355X.
+
+One step = one pass of the whole hot path on one batch: quantize X to MXFP4,
+form the fp32 residual and quantize it (one kernel), then the K-doubled
+block-scaled FP4 GEMM into Y (one kernel). The weight is quantized once
+before timing (setup). Inputs are seeded synthetic tensors already resident
+in HBM when the timed region starts.
+
+Workload: the Wan2.2-DiT-style FFN layer, X [4096, 5120] bf16 (Laplace(0,1)
+with 8 outlier channels x80), W [13824, 5120] quantized to MXFP4, Y bf16.
+
+Prints one JSON line (rank 0) with the effective TFLOP/s of the step
+(4 M N K per step: the contraction over the doubled K), the per-kernel
+rooflines measured with HIP events on the launch stream, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA, TFLOP/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "RFQ W4A4 linear effective TFLOP/s (% MXFP4 peak); quantize GB/s (% HBM)"
+QUANT_BYTES_PER_ELEM = 2 + 2 * (0.5 + 1.0 / 32)      # bf16 in, Q(X) and Q(R) codes + scales out
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="wan22_ffn")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--no-hbm-quantize", action="store_true",
+                    help="skip the extra quantize measurement on the long-sequence layer")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mxfp4_activation_gemm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, kernel_hash):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"gemm_counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_hash:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(cfg):
+    """The oracle, as it stands, on a bounded sample of the workload; the
+    full-size time is extrapolated from per-row quantization time and
+    per-output GEMM time (labelled as such)."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    q_rows, g_rows, g_cols = 512, 256, 2048
+    x = oracle.bf16_bits_to_f64(workloads.x_bf16(cfg, 0, q_rows))
+    w = oracle.bf16_bits_to_f64(workloads.w_bf16(cfg)[:g_cols])
+    wq, sw = oracle.quantize_mxfp4(w)                      # setup, as on the GPU
+    t0 = time.perf_counter()
+    qx, sx, qr, sr = oracle.residual_quantize(x)
+    t_q = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gemm_w4a4(qx[:g_rows], sx[:g_rows], qr[:g_rows], sr[:g_rows], wq, sw)
+    t_g = time.perf_counter() - t0
+    t_full = t_q / q_rows * cfg.M + t_g / (g_rows * g_cols) * cfg.M * cfg.N
+    value = 4.0 * cfg.M * cfg.N * cfg.K / t_full / 1e12
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"oracle residual_quantize on {q_rows} rows of X ({t_q:.2f} s, 1 thread) and oracle "
+                   f"K-doubled float64 GEMM on {g_rows} rows x {g_cols} columns ({t_g:.2f} s, "
+                   f"{blas_threads} BLAS threads); full {cfg.M}x{cfg.N}x{cfg.K} time extrapolated to "
+                   f"{t_full:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by rows of X with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    import mxfp4_activation_gemm_amd as rfq
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rfq.library()
+    cfg = workloads.CONFIGS[args.workload]
+    M, N, K = cfg.M, cfg.N, cfg.K
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = to_dev(workloads.x_bf16(cfg))
+    w = to_dev(workloads.w_bf16(cfg))
+    wq, sw = rfq.quantize_mxfp4(w)                 # setup: the weight is quantized once
+    del w
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    qr = torch.empty_like(qx)
+    sx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    sr = torch.empty_like(sx)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    lib = rfq.library()
+    stream = torch.cuda.current_stream()
+    sp = rfq._stream()
+
+    def step(ev=None):
+        # the two launches of rfq_linear, with events between them
+        if ev is not None:
+            ev[0].record(stream)
+        rfq._lib.check(lib.rfq_residual_quantize(x.data_ptr(), 0, M, K, x.stride(0), qx.data_ptr(), sx.data_ptr(),
+                                                 qr.data_ptr(), sr.data_ptr(), sp))
+        if ev is not None:
+            ev[1].record(stream)
+        rfq._lib.check(lib.rfq_gemm_w4a4(qx.data_ptr(), sx.data_ptr(), qr.data_ptr(), sr.data_ptr(), wq.data_ptr(),
+                                         sw.data_ptr(), M, N, K, y.data_ptr(), rfq._lib.DTYPE_BF16, N, sp))
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+
+    flops = 4.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    quant_gbs = QUANT_BYTES_PER_ELEM * M * K / (quant_ms * 1e-3) / 1e9
+
+    # plain W4A4 GEMM (no residual operand) on the same operands, for the
+    # overhead of the residual path
+    for _ in range(5):
+        rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out=y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(50):
+        rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    w4a4_ms = e0.elapsed_time(e1) / 50
+
+    kernel_hash = source_hash("gemm.hip")
+    traffic = counter_traffic(args.workload, kernel_hash)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "M": M, "N": N, "K": K,
+            "x_dtype": "bf16", "y_dtype": "bf16",
+            "flops_per_step": flops,
+            "pct_fp4_peak_whole_step": round(100 * value / FP4_PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "rfq_gemm_w4a4 (K-doubled FP4 GEMM)",
+            "achieved": round(gemm_tflops, 2),
+            "peak": FP4_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gemm_ms * 1e3, 2),
+        },
+        "kernels": {
+            "quantize_residual": {
+                "avg_launch_us": round(quant_ms * 1e3, 2),
+                "GB_per_s": round(quant_gbs, 1),
+                "pct_hbm_peak": round(100 * quant_gbs / HBM_PEAK_GBS, 2),
+                "algorithmic_bytes": QUANT_BYTES_PER_ELEM * M * K,
+            },
+            "gemm_rfq": {
+                "avg_launch_us": round(gemm_ms * 1e3, 2),
+                "TFLOP_per_s": round(gemm_tflops, 1),
+                "pct_fp4_peak": round(100 * gemm_tflops / FP4_PEAK_TFLOPS, 2),
+            },
+            "gemm_plain_w4a4": {
+                "avg_launch_us": round(w4a4_ms * 1e3, 2),
+                "TFLOP_per_s_2MNK": round(2.0 * M * N * K / (w4a4_ms * 1e-3) / 1e12, 1),
+                "rfq_over_w4a4_time": round(gemm_ms / w4a4_ms, 3),
+            },
+        },
+    }
+    del qx, qr, sx, sr, y, x
+
+    if not args.no_hbm_quantize:
+        # the quantize pass on the long-sequence layer, whose traffic (1.39 GB)
+        # exceeds the 256 MB last-level cache, so the figure is HBM-bound
+        c5 = workloads.CONFIGS["dit_ffn_down"]
+        x5 = to_dev(workloads.x_bf16(c5))
+        q5 = [torch.empty((c5.M, c5.K // 2), dtype=torch.uint8, device=dev) for _ in range(2)]
+        s5 = [torch.empty((c5.M, c5.K // 32), dtype=torch.uint8, device=dev) for _ in range(2)]
+
+        def q5_step():
+            rfq._lib.check(lib.rfq_residual_quantize(x5.data_ptr(), 0, c5.M, c5.K, c5.K, q5[0].data_ptr(),
+                                                     s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
+        for _ in range(3):
+            q5_step()
+        e0.record(stream)
+        reps = 20
+        for _ in range(reps):
+            q5_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        q5_ms = e0.elapsed_time(e1) / reps
+        gbs = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5_ms * 1e-3) / 1e9
+        out["kernels"]["quantize_residual_dit_ffn_down"] = {
+            "shape": [c5.M, c5.K],
+            "avg_launch_us": round(q5_ms * 1e3, 2),
+            "GB_per_s": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        }
+        del x5, q5, s5
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = a.numel()
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

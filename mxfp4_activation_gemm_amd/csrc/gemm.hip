@@ -46,26 +46,39 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;
-constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kWavesM = 2, kWavesN = 2;
-constexpr int kTM = kBM / kWavesM / 32;     // 4 MFMA tiles along M per wave
-constexpr int kTN = kBN / kWavesN / 32;     // 4 along N
+constexpr int kThreads = 256;               // 4 waves per workgroup
+constexpr int kBK = 128;                    // K elements per stage
 constexpr int kSteps = kBK / 64;            // 2 MFMA K-steps per stage
 constexpr int kRowBytes = kBK / 2;          // 64 bytes of codes per row per stage
-constexpr int kTileBytesA = kBM * kRowBytes;           // 16 KB
-constexpr int kTileBytesB = kBN * kRowBytes;           // 16 KB
-constexpr int kStageBytes = 2 * kTileBytesA + kTileBytesB;  // X, R, W
 constexpr int kScaleGroup = 4;              // stages per scale fetch (16 blocks)
 constexpr int kScaleRowBytes = 16;
-constexpr int kScaleBytesA = kBM * kScaleRowBytes;     // 4 KB
-constexpr int kScaleBytes = 2 * kScaleBytesA + kBN * kScaleRowBytes;
-constexpr int kLdsBytes = 2 * kStageBytes + 2 * kScaleBytes;   // 120 KB
 constexpr uint32_t kOOB = 0x80000000u;      // voffset that is always out of range
 constexpr int kGroupM = 4;                  // tile rows swept together (L2 reuse)
-constexpr int kLoadsPerTile = kBM / 16 / 4; // 16-row load instructions per wave per tile (4)
 
-static_assert(kBM == kBN, "the load distribution below assumes square tiles");
+// Output tile BM x BN on a kWavesM x kWavesN grid of waves; kOcc workgroups
+// are meant to share a CU (LDS and registers are sized for that).
+template <int BM_, int BN_, int WavesM_, int WavesN_, int Occ_>
+struct TileCfg {
+  static constexpr int kBM = BM_, kBN = BN_, kWavesM = WavesM_, kWavesN = WavesN_, kOcc = Occ_;
+  static_assert(kWavesM * kWavesN * 64 == kThreads, "4 waves");
+  static constexpr int kTM = kBM / kWavesM / 32;   // MFMA tiles along M per wave
+  static constexpr int kTN = kBN / kWavesN / 32;   // along N
+  static constexpr int kTileBytesA = kBM * kRowBytes;
+  static constexpr int kTileBytesB = kBN * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytesA + kTileBytesB;     // X, R, W
+  static constexpr int kScaleBytesA = kBM * kScaleRowBytes;
+  static constexpr int kScaleBytes = 2 * kScaleBytesA + kBN * kScaleRowBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes + 2 * kScaleBytes;
+  static constexpr int kLoadsA = kBM / 4 / 16;     // 16-row load instructions per wave for X (and R)
+  static constexpr int kLoadsB = kBN / 4 / 16;     // for W
+  static constexpr int kScaleLoadsA = kBM / 64;    // 64-row scale instructions per operand
+  static constexpr int kScaleLoadsB = kBN / 64;
+  static constexpr int kScaleLoads = 2 * kScaleLoadsA + kScaleLoadsB;
+  static_assert(kScaleLoads % 4 == 0, "scale loads spread evenly over 4 waves");
+  static_assert(kLdsBytes * kOcc <= 160 * 1024, "LDS budget per CU");
+};
+using Tile256 = TileCfg<256, 256, 2, 2, 1>;   // one workgroup per CU, 128x128 per wave
+using Tile128 = TileCfg<128, 256, 2, 2, 2>;   // two workgroups per CU, 64x128 per wave
 
 struct GemmParams {
   const uint8_t* qx;
@@ -114,7 +127,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = in_group / gsize;
 }
 
-template <int S, bool kResid>
+template <int S, bool kResid, int kTM, int kTN>
 __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x8_t (&ax)[kTM],
                                           const i32x8_t (&ar)[kTM], const i32x8_t (&b)[kTN],
                                           const uint32_t (&scx)[kTM], const uint32_t (&scr)[kTM],
@@ -136,9 +149,13 @@ __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x8
 }
 
 // kFast: K % 512 == 0 (whole stages and whole 16-block scale groups).
-template <bool kResid, bool kOutBf16, bool kFast>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+template <class C, bool kResid, bool kOutBf16, bool kFast>
+__global__ __launch_bounds__(kThreads, C::kOcc) void gemm_kernel(GemmParams p) {
+  constexpr int kBM = C::kBM, kBN = C::kBN, kWavesM = C::kWavesM, kWavesN = C::kWavesN;
+  constexpr int kTM = C::kTM, kTN = C::kTN;
+  constexpr int kTileBytesA = C::kTileBytesA, kStageBytes = C::kStageBytes;
+  constexpr int kScaleBytesA = C::kScaleBytesA, kScaleBytes = C::kScaleBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
   uint8_t* const tiles = lds;
   uint8_t* const scales = lds + 2 * kStageBytes;
 
@@ -158,29 +175,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rsr = make_rsrc(kResid ? p.sr + (int64_t)m0 * kblocks : p.sx, rows_a * kblocks);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
 
-  // Code-tile loads: this wave fetches tile rows [64 wave, 64 wave + 64) of
-  // each operand, 16 rows per instruction; lane l takes row 16 n + l / 4 and
-  // chunk (l % 4) ^ f(row) of it.
+  // Code-tile loads: this wave fetches tile rows [BM/4 wave, BM/4 (wave+1))
+  // of X and R and [BN/4 wave, BN/4 (wave+1)) of W, 16 rows per instruction;
+  // lane l takes row 16 n + l / 4 and chunk (l % 4) ^ f(row) of it.
   const unsigned lrow = lane & 31, lhalf = lane >> 5;
-  uint32_t ld_voff[kLoadsPerTile];
-  uint32_t ld_chunk[kLoadsPerTile];
+  uint32_t lda_voff[C::kLoadsA], lda_chunk[C::kLoadsA], ldb_voff[C::kLoadsB], ldb_chunk[C::kLoadsB];
 #pragma unroll
-  for (int n = 0; n < kLoadsPerTile; ++n) {
-    const uint32_t row = 64 * wave + 16 * n + (lane >> 2);
-    ld_chunk[n] = (lane & 3) ^ swz(row);
-    ld_voff[n] = row * kbytes + 16 * ld_chunk[n];
+  for (int n = 0; n < C::kLoadsA; ++n) {
+    const uint32_t row = kBM / 4 * wave + 16 * n + (lane >> 2);
+    lda_chunk[n] = (lane & 3) ^ swz(row);
+    lda_voff[n] = row * kbytes + 16 * lda_chunk[n];
+  }
+#pragma unroll
+  for (int n = 0; n < C::kLoadsB; ++n) {
+    const uint32_t row = kBN / 4 * wave + 16 * n + (lane >> 2);
+    ldb_chunk[n] = (lane & 3) ^ swz(row);
+    ldb_voff[n] = row * kbytes + 16 * ldb_chunk[n];
   }
 
   auto issue_stage = [&](int st, uint8_t* buf) {
     const uint32_t kb = (uint32_t)st * kRowBytes;
 #pragma unroll
-    for (int n = 0; n < kLoadsPerTile; ++n) {
-      uint32_t vo = ld_voff[n] + kb;
-      if (!kFast && (uint32_t)st * (kBK / 32) + ld_chunk[n] >= kblocks) vo = kOOB;
-      uint8_t* dst = buf + (64 * wave + 16 * n) * kRowBytes;
+    for (int n = 0; n < C::kLoadsA; ++n) {
+      uint32_t vo = lda_voff[n] + kb;
+      if (!kFast && (uint32_t)st * (kBK / 32) + lda_chunk[n] >= kblocks) vo = kOOB;
+      uint8_t* dst = buf + (kBM / 4 * wave + 16 * n) * kRowBytes;
       load16_to_lds(rx, dst, vo);
       if (kResid) load16_to_lds(rr, dst + kTileBytesA, vo);
-      load16_to_lds(rw, dst + 2 * kTileBytesA, vo);
+    }
+#pragma unroll
+    for (int n = 0; n < C::kLoadsB; ++n) {
+      uint32_t vo = ldb_voff[n] + kb;
+      if (!kFast && (uint32_t)st * (kBK / 32) + ldb_chunk[n] >= kblocks) vo = kOOB;
+      load16_to_lds(rw, buf + 2 * kTileBytesA + (kBN / 4 * wave + 16 * n) * kRowBytes, vo);
     }
   };
 
@@ -209,18 +236,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             i32x4_t{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
       }
   };
+  // Instruction j of a group covers 64 rows: j < A loads X rows, then R rows,
+  // then W rows (A = BM / 64); wave w issues j = w q .. w q + q - 1.
   auto issue_scales = [&](int g, uint8_t* sbuf) {
+    constexpr int kA = C::kScaleLoadsA, kPerWave = C::kScaleLoads / 4;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int j = 3 * (int)wave + q;   // wave-uniform: plain branches, no descriptor select
-      const uint32_t row = 64 * (j % 4) + lane;
-      uint8_t* dst = sbuf + (j / 4) * kScaleBytesA + 64 * (j % 4) * kScaleRowBytes;
-      if (j < 4)
-        issue_scale_rows(rsx, g, dst, row);
-      else if (j < 8) {
-        if (kResid) issue_scale_rows(rsr, g, dst, row);
-      } else
-        issue_scale_rows(rsw, g, dst, row);
+    for (int q = 0; q < kPerWave; ++q) {
+      const int j = kPerWave * (int)wave + q;   // wave-uniform: plain branches, no descriptor select
+      if (j < kA) {
+        issue_scale_rows(rsx, g, sbuf + 64 * j * kScaleRowBytes, 64 * j + lane);
+      } else if (j < 2 * kA) {
+        if (kResid) issue_scale_rows(rsr, g, sbuf + kScaleBytesA + 64 * (j - kA) * kScaleRowBytes, 64 * (j - kA) + lane);
+      } else {
+        issue_scale_rows(rsw, g, sbuf + 2 * kScaleBytesA + 64 * (j - 2 * kA) * kScaleRowBytes, 64 * (j - 2 * kA) + lane);
+      }
     }
   };
 
@@ -240,6 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   const int nstages = (p.K + kBK - 1) / kBK;
+  i32x4_t gx[kTM], gr[kTM], gw[kTN];     // scale rows of the current group
   issue_scales(0, scales);
   issue_stage(0, tiles);
 
@@ -261,27 +291,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < kTN; ++j) bw[s][j] = read_frag(buf + 2 * kTileBytesA + (b_row0 + 32 * j) * kRowBytes + rd_off[s]);
     }
-    // Scale words of this stage: byte 2 s of (word >> 8 lhalf) is the scale of
-    // block 4 st + 2 s + lhalf of the lane's row.
-    const uint32_t sofs = (st % kScaleGroup) * 4;
+    // Scale words: every fourth stage each lane reads the 16 bytes (16
+    // blocks = 4 stages) of each of its rows in one ds_read_b128; word
+    // (st % 4) of them serves stage st, and byte 2 s of (word >> 8 lhalf) is
+    // the scale of block 4 st + 2 s + lhalf of the row.
+    if (st % kScaleGroup == 0) {
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const uint8_t* s0 = sbuf + (a_row0 + 32 * i + lrow) * kScaleRowBytes;
+        gx[i] = *reinterpret_cast<const i32x4_t*>(s0);
+        if (kResid) gr[i] = *reinterpret_cast<const i32x4_t*>(s0 + kScaleBytesA);
+      }
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+        gw[j] = *reinterpret_cast<const i32x4_t*>(sbuf + 2 * kScaleBytesA + (b_row0 + 32 * j + lrow) * kScaleRowBytes);
+    }
+    const int sw_idx = st % kScaleGroup;
     uint32_t cx[kTM], cr[kTM], cw[kTN];
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const uint8_t* s0 = sbuf + (a_row0 + 32 * i + lrow) * kScaleRowBytes + sofs;
-      cx[i] = *reinterpret_cast<const uint32_t*>(s0) >> (8 * lhalf);
-      cr[i] = kResid ? *reinterpret_cast<const uint32_t*>(s0 + kScaleBytesA) >> (8 * lhalf) : 0u;
+      cx[i] = (uint32_t)gx[i][sw_idx] >> (8 * lhalf);
+      cr[i] = kResid ? (uint32_t)gr[i][sw_idx] >> (8 * lhalf) : 0u;
     }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j)
-      cw[j] = *reinterpret_cast<const uint32_t*>(sbuf + 2 * kScaleBytesA + (b_row0 + 32 * j + lrow) * kScaleRowBytes +
-                                                 sofs) >> (8 * lhalf);
+    for (int j = 0; j < kTN; ++j) cw[j] = (uint32_t)gw[j][sw_idx] >> (8 * lhalf);
 
     if (st + 1 < nstages) {
       if ((st + 1) % kScaleGroup == 0) issue_scales((st + 1) / kScaleGroup, scales + (((st + 1) / kScaleGroup) & 1) * kScaleBytes);
       issue_stage(st + 1, tiles + ((st + 1) & 1) * kStageBytes);
     }
-    mfma_step<0, kResid>(acc, ax[0], ar[0], bw[0], cx, cr, cw);
-    mfma_step<1, kResid>(acc, ax[1], ar[1], bw[1], cx, cr, cw);
+    mfma_step<0, kResid, kTM, kTN>(acc, ax[0], ar[0], bw[0], cx, cr, cw);
+    mfma_step<1, kResid, kTM, kTN>(acc, ax[1], ar[1], bw[1], cx, cr, cw);
   }
 
   // Epilogue: fp32 accumulators to Y.
@@ -309,13 +349,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-template <bool kResid, bool kOutBf16>
-hipError_t launch_variant(const GemmParams& p, bool fast, int grid, hipStream_t stream) {
+template <class C, bool kResid, bool kOutBf16>
+hipError_t launch_variant(GemmParams p, bool fast, hipStream_t stream) {
+  p.tiles_m = (p.M + C::kBM - 1) / C::kBM;
+  p.tiles_n = (p.N + C::kBN - 1) / C::kBN;
+  const int grid = p.tiles_m * p.tiles_n;
   if (fast)
-    hipLaunchKernelGGL((gemm_kernel<kResid, kOutBf16, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<kResid, kOutBf16, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmParams& p, bool resid, bool y_bf16, bool fast, hipStream_t stream) {
+  if (resid)
+    return y_bf16 ? launch_variant<C, true, true>(p, fast, stream) : launch_variant<C, true, false>(p, fast, stream);
+  return y_bf16 ? launch_variant<C, false, true>(p, fast, stream) : launch_variant<C, false, false>(p, fast, stream);
 }
 
 }  // namespace
@@ -327,16 +377,8 @@ hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, 
   p.qx = qx; p.sx = sx; p.qr = qr; p.sr = sr; p.w = w; p.sw = sw;
   p.y = y; p.ldy = ldy;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
-  p.tiles_m = (int32_t)((M + kBM - 1) / kBM);
-  p.tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  const int grid = p.tiles_m * p.tiles_n;
   const bool fast = (K % (kBK * kScaleGroup)) == 0;
-  const bool resid = qr != nullptr;
-  if (resid)
-    return y_bf16 ? launch_variant<true, true>(p, fast, grid, stream)
-                  : launch_variant<true, false>(p, fast, grid, stream);
-  return y_bf16 ? launch_variant<false, true>(p, fast, grid, stream)
-                : launch_variant<false, false>(p, fast, grid, stream);
+  return launch_cfg<Tile128>(p, qr != nullptr, y_bf16, fast, stream);
 }
 
 }  // namespace rfq
