@@ -14,71 +14,79 @@
 // the E8M0 code of that (row, block) in the byte chosen by op_sel. Output
 // lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4.
 //
-// Tiling: a 256 x 256 output tile per workgroup of 4 waves (2 x 2), each
-// wave 128 x 128 = 4 x 4 MFMA tiles (256 fp32 accumulators per lane).
-// K advances 128 elements (64 bytes of codes per row) per stage, two MFMA
-// steps.
+// Tiling: a 256 x 256 output tile per workgroup of 4 waves on a 2 x 2 grid,
+// one wave per SIMD; each wave owns 128 x 128 outputs = 4 x 4 MFMA tiles
+// (256 fp32 accumulators per lane, in AGPRs). K advances 128 elements (64
+// bytes of codes per row) per stage, as two MFMA steps.
 //
-// Data movement, per stage:
-//  * Code tiles (QX, QR, W; 256 rows x 64 B each) go global -> LDS with
-//    buffer loads that write LDS directly. Four consecutive lanes fetch one
-//    row's 64 contiguous bytes, so each quad touches one cache line. In LDS a
-//    row is 4 chunks of 16 B (one K-block each); chunk c of row r sits at
-//    position c ^ f(r), f(r) = (r >> 2) & 3, which makes the MFMA operand
-//    reads (32 rows, same chunk) free of LDS bank conflicts on gfx950
-//    (measured with the LDS bank-conflict counter; swizzles that are
-//    conflict-free under a plain 32- or 64-bank model were not). The swizzle
-//    is applied by choosing which chunk each lane fetches; the LDS slot of a
-//    lane is fixed by the hardware.
-//  * Scales are fetched 16 B per row (16 blocks = 4 stages) into a separate
-//    LDS area every fourth stage; each stage reads its 4-byte word per row.
+// Data movement:
+//  * Code tiles (QX, QR, W; 256 rows x 64 B each per stage) go global ->
+//    LDS with buffer loads that write LDS directly. Four consecutive lanes
+//    fetch one row's 64 contiguous bytes, so each quad touches one cache
+//    line. In LDS a row is 4 chunks of 16 B (one K-block each); chunk c of
+//    row r sits at position c ^ f(r), f(r) = (r >> 2) & 3, which keeps the
+//    MFMA operand reads (32 rows, same chunk) free of LDS bank conflicts on
+//    gfx950 (measured with the bank-conflict counter). The swizzle is applied
+//    by choosing which chunk each lane fetches.
+//  * Stages live in a ring of three LDS buffers and are fetched two stages
+//    ahead, so a fetch that misses L2 has two stages of MFMA work to land.
+//    Each wait names exactly the loads it needs (s_waitcnt vmcnt(N) with N =
+//    the loads issued after them), never "everything outstanding".
+//  * Scales: 16 bytes per row (16 blocks = 4 stages) per scale group, in one
+//    LDS buffer; each lane copies its rows into registers once per group, and
+//    the next group is fetched as soon as every wave has done so.
+//  * Within a stage, the second MFMA step's fragments are read while the
+//    first step's MFMAs run, and the next stage's first-step fragments while
+//    the second step's run; one barrier per stage sits between the two.
 //  * Buffer loads return zero outside the tensor, which covers partial M
 //    and N tiles; partial K is masked per 16-byte chunk.
-// Two LDS stages: stage s + 1 is loaded while stage s's 64 MFMAs run.
 
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace rfq {
 namespace {
 
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;               // 4 waves per workgroup
-constexpr int kBK = 128;                    // K elements per stage
-constexpr int kSteps = kBK / 64;            // 2 MFMA K-steps per stage
-constexpr int kRowBytes = kBK / 2;          // 64 bytes of codes per row per stage
-constexpr int kScaleGroup = 4;              // stages per scale fetch (16 blocks)
+constexpr int kBK = 128;                            // K elements per stage
+constexpr int kWavesN = 2;                          // wave grid (waves / 2) x 2
+constexpr int kRowBytes = kBK / 2;                  // 64 bytes of codes per row per stage
+constexpr int kRing = 3;                            // LDS stages in flight
+constexpr int kScaleGroup = 4;                      // stages per scale fetch (16 blocks)
 constexpr int kScaleRowBytes = 16;
-constexpr uint32_t kOOB = 0x80000000u;      // voffset that is always out of range
-constexpr int kGroupM = 4;                  // tile rows swept together (L2 reuse)
+constexpr uint32_t kOOB = 0x80000000u;              // voffset that is always out of range
+constexpr int kGroupM = 4;                          // tile rows swept together (L2 reuse)
 
-// Output tile BM x BN on a kWavesM x kWavesN grid of waves; kOcc workgroups
-// are meant to share a CU (LDS and registers are sized for that).
-template <int BM_, int BN_, int WavesM_, int WavesN_, int Occ_>
+// An output tile of BM x BN on `Waves` waves (grid Waves/2 x 2); Occ
+// workgroups are meant to share a CU, and LDS and registers are sized so.
+template <int BM_, int BN_, int Waves_, int Occ_>
 struct TileCfg {
-  static constexpr int kBM = BM_, kBN = BN_, kWavesM = WavesM_, kWavesN = WavesN_, kOcc = Occ_;
-  static_assert(kWavesM * kWavesN * 64 == kThreads, "4 waves");
-  static constexpr int kTM = kBM / kWavesM / 32;   // MFMA tiles along M per wave
-  static constexpr int kTN = kBN / kWavesN / 32;   // along N
-  static constexpr int kTileBytesA = kBM * kRowBytes;
-  static constexpr int kTileBytesB = kBN * kRowBytes;
-  static constexpr int kStageBytes = 2 * kTileBytesA + kTileBytesB;     // X, R, W
+  static constexpr int kBM = BM_, kBN = BN_, kWaves = Waves_, kOcc = Occ_;
+  static constexpr int kWavesM = kWaves / kWavesN;
+  static constexpr int kWaveM = kBM / kWavesM, kWaveN = kBN / kWavesN;
+  static constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;           // MFMA tiles per wave
+  static constexpr int kTileBytesA = kBM * kRowBytes, kTileBytesB = kBN * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytesA + kTileBytesB;    // X, R, W
   static constexpr int kScaleBytesA = kBM * kScaleRowBytes;
   static constexpr int kScaleBytes = 2 * kScaleBytesA + kBN * kScaleRowBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes + 2 * kScaleBytes;
-  static constexpr int kLoadsA = kBM / 4 / 16;     // 16-row load instructions per wave for X (and R)
-  static constexpr int kLoadsB = kBN / 4 / 16;     // for W
-  static constexpr int kScaleLoadsA = kBM / 64;    // 64-row scale instructions per operand
-  static constexpr int kScaleLoadsB = kBN / 64;
-  static constexpr int kScaleLoads = 2 * kScaleLoadsA + kScaleLoadsB;
-  static_assert(kScaleLoads % 4 == 0, "scale loads spread evenly over 4 waves");
+  static constexpr int kLdsBytes = kRing * kStageBytes + kScaleBytes;
+  static constexpr int kLoadsA = kBM / 16 / kWaves;    // 16-row DMA instructions per wave for X (and R)
+  static constexpr int kLoadsB = kBN / 16 / kWaves;    // for W
+  static_assert(kTM >= 1 && kTN >= 1 && kLoadsA >= 1 && kLoadsB >= 1, "tile shape");
   static_assert(kLdsBytes * kOcc <= 160 * 1024, "LDS budget per CU");
 };
-using Tile256 = TileCfg<256, 256, 2, 2, 1>;   // one workgroup per CU, 128x128 per wave
-using Tile128 = TileCfg<128, 256, 2, 2, 2>;   // two workgroups per CU, 64x128 per wave
+// 256 x 256 outputs, 8 waves of 64 x 128 (128 accumulators each), one
+// workgroup per CU, 156 KB of LDS: the main tile.
+using BigTile = TileCfg<256, 256, 8, 1>;
+// 128 x 128 outputs, 4 waves of 64 x 64, two workgroups per CU (78 KB of LDS
+// each): quadrants of big tiles, for the last partial round of a launch.
+using QuadTile = TileCfg<128, 128, 4, 2>;
 
 struct GemmParams {
   const uint8_t* qx;
@@ -90,7 +98,12 @@ struct GemmParams {
   void* y;
   int64_t ldy;
   int32_t M, N, K;
-  int32_t tiles_m, tiles_n;
+  // Tile map: `grid` workgroups; tiles of gm x gn form a tiles_m x tiles_n
+  // grid walked in a fixed logical order; workgroup ids map to logical tile
+  // first + (0 .. grid - 1), or with `quadrants` to quadrant (id % 4) of
+  // logical tile first + id / 4.
+  int32_t tiles_m, tiles_n, gm, gn;
+  int32_t first, grid, quadrants;
 };
 
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 2) & 3u; }
@@ -104,67 +117,113 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
-__device__ __forceinline__ i32x8_t read_frag(const uint8_t* p) {
-  const i32x4_t v = *reinterpret_cast<const i32x4_t*>(p);
-  return i32x8_t{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+__device__ __forceinline__ i32x4_t read_frag(const uint8_t* p) { return *reinterpret_cast<const i32x4_t*>(p); }
+
+// FP4 operands use the low 4 of the instruction's 8 operand registers.
+__device__ __forceinline__ i32x8_t widen(i32x4_t v) { return i32x8_t{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
+
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima); gfx9
+// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+
+// Barrier without the workgroup memory fence that __syncthreads implies (that
+// fence would also wait for the loads of later stages still in flight). LDS
+// reads and writes of this wave are complete before it (lgkmcnt(0) above the
+// call sites); the compiler barriers keep memory accesses from moving across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// Maps a workgroup id to an output tile: first spread consecutive tiles of
-// one XCD's share over its workgroups (ids are dealt round-robin to the 8
-// XCDs), then walk tiles in groups of kGroupM tile rows so that concurrently
-// running workgroups share activation rows and weight columns in L2.
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
+// Maps a workgroup id to the origin of its output tile. Ids are dealt
+// round-robin to the 8 XCDs, so consecutive logical tiles are first spread
+// over one XCD's share of ids; logical tiles are then walked in groups of
+// kGroupM tile rows, so that concurrently running workgroups share
+// activation rows and weight columns in that XCD's L2.
+__device__ __forceinline__ void tile_origin(const GemmParams& p, int bid, int& m0, int& n0) {
+  const int total = p.grid;
   const int xcd = bid % 8, idx = bid / 8;
   const int base = total / 8, rem = total % 8;
-  const int logical = xcd < rem ? xcd * (base + 1) + idx : rem * (base + 1) + (xcd - rem) * base + idx;
-  const int per_group = kGroupM * tiles_n;
+  const int local = xcd < rem ? xcd * (base + 1) + idx : rem * (base + 1) + (xcd - rem) * base + idx;
+  const int logical = p.first + (p.quadrants ? local / 4 : local);
+  const int q = p.quadrants ? local % 4 : 0;
+  const int per_group = kGroupM * p.tiles_n;
   const int group = logical / per_group;
   const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int gsize = min(p.tiles_m - first_m, kGroupM);
   const int in_group = logical - group * per_group;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
+  const int tm = first_m + in_group % gsize, tn = in_group / gsize;
+  m0 = tm * p.gm + (q / 2) * (p.gm / 2);
+  n0 = tn * p.gn + (q % 2) * (p.gn / 2);
 }
 
 template <int S, bool kResid, int kTM, int kTN>
-__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x8_t (&ax)[kTM],
-                                          const i32x8_t (&ar)[kTM], const i32x8_t (&b)[kTN],
+__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x4_t (&ax)[kTM],
+                                          const i32x4_t (&ar)[kTM], const i32x4_t (&b)[kTN],
                                           const uint32_t (&scx)[kTM], const uint32_t (&scr)[kTM],
                                           const uint32_t (&scw)[kTN]) {
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ax[i], b[j], acc[i][j], 4, 4, 2 * S,
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ax[i]), widen(b[j]), acc[i][j], 4, 4, 2 * S,
                                                                   (int)scx[i], 2 * S, (int)scw[j]);
   if (kResid) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ar[i], b[j], acc[i][j], 4, 4, 2 * S,
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ar[i]), widen(b[j]), acc[i][j], 4, 4, 2 * S,
                                                                     (int)scr[i], 2 * S, (int)scw[j]);
   }
 }
 
-// kFast: K % 512 == 0 (whole stages and whole 16-block scale groups).
+// Scheduling hint for one MFMA step of kMfma MFMAs: spread the step's
+// LDS-DMA loads (kVmem) and LDS reads (kReads) evenly behind the MFMAs, so
+// that they issue while the MFMA pipe is busy instead of in a block.
+template <int kSlot, int kMfma, int kVmem, int kReads>
+__device__ __forceinline__ void interleave_slots() {
+  if constexpr (kSlot < kMfma) {
+    constexpr int vm = ((kSlot + 1) * kVmem) / kMfma - (kSlot * kVmem) / kMfma;
+    constexpr int ds = ((kSlot + 1) * kReads) / kMfma - (kSlot * kReads) / kMfma;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+    if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x010, vm, 0);   // any VMEM (the LDS-DMA loads)
+    if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);   // DS read
+    interleave_slots<kSlot + 1, kMfma, kVmem, kReads>();
+  }
+}
+template <int kReads, int kVmem, int kMfma>
+__device__ __forceinline__ void interleave_hint() {
+  interleave_slots<0, kMfma, kVmem, kReads>();
+}
+
+// kFast: K % 512 == 0 (whole stages and whole 16-block scale groups); the
+// other instantiation masks partial K and waits for all loads at each stage.
 template <class C, bool kResid, bool kOutBf16, bool kFast>
-__global__ __launch_bounds__(kThreads, C::kOcc) void gemm_kernel(GemmParams p) {
-  constexpr int kBM = C::kBM, kBN = C::kBN, kWavesM = C::kWavesM, kWavesN = C::kWavesN;
-  constexpr int kTM = C::kTM, kTN = C::kTN;
+__global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParams p) {
+  constexpr int kBM = C::kBM, kBN = C::kBN, kWaves = C::kWaves;
+  constexpr int kWaveM = C::kWaveM, kWaveN = C::kWaveN, kTM = C::kTM, kTN = C::kTN;
   constexpr int kTileBytesA = C::kTileBytesA, kStageBytes = C::kStageBytes;
-  constexpr int kScaleBytesA = C::kScaleBytesA, kScaleBytes = C::kScaleBytes;
+  constexpr int kScaleBytesA = C::kScaleBytesA;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
-  uint8_t* const tiles = lds;
-  uint8_t* const scales = lds + 2 * kStageBytes;
+  uint8_t* const ring = lds;
+  uint8_t* const sbuf = lds + kRing * kStageBytes;
 
   const unsigned lane = threadIdx.x & 63;
-  const unsigned wave = threadIdx.x >> 6;
+  // wave index as a scalar: everything derived from it (row ranges, which
+  // operand a scale piece belongs to) stays in SGPRs and scalar branches
+  const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const unsigned wm = wave / kWavesN, wn = wave % kWavesN;
-  int tm, tn;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const unsigned lrow = lane & 31, lhalf = lane >> 5;
+  int m0, n0;
+  tile_origin(p, blockIdx.x, m0, n0);
+  if (m0 >= p.M || n0 >= p.N) return;   // a quadrant past the edge (whole workgroup)
   const uint32_t kbytes = (uint32_t)p.K / 2, kblocks = (uint32_t)p.K / 32;
   const uint32_t rows_a = (uint32_t)min(kBM, p.M - m0), rows_b = (uint32_t)min(kBN, p.N - n0);
 
@@ -175,90 +234,129 @@ __global__ __launch_bounds__(kThreads, C::kOcc) void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rsr = make_rsrc(kResid ? p.sr + (int64_t)m0 * kblocks : p.sx, rows_a * kblocks);
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
 
-  // Code-tile loads: this wave fetches tile rows [BM/4 wave, BM/4 (wave+1))
-  // of X and R and [BN/4 wave, BN/4 (wave+1)) of W, 16 rows per instruction;
-  // lane l takes row 16 n + l / 4 and chunk (l % 4) ^ f(row) of it.
-  const unsigned lrow = lane & 31, lhalf = lane >> 5;
+  const int nstages = (p.K + kBK - 1) / kBK;
+  const int ngroups = (nstages + kScaleGroup - 1) / kScaleGroup;
+
+  // Code-tile loads: wave w fetches rows [BM/waves w, BM/waves (w + 1)) of X
+  // and R and the matching range of W's BN rows, 16 rows per instruction;
+  // lane l takes row 16 n + l / 4 of them and chunk (l % 4) ^ f(row).
   uint32_t lda_voff[C::kLoadsA], lda_chunk[C::kLoadsA], ldb_voff[C::kLoadsB], ldb_chunk[C::kLoadsB];
 #pragma unroll
   for (int n = 0; n < C::kLoadsA; ++n) {
-    const uint32_t row = kBM / 4 * wave + 16 * n + (lane >> 2);
+    const uint32_t row = kBM / kWaves * wave + 16 * n + (lane >> 2);
     lda_chunk[n] = (lane & 3) ^ swz(row);
     lda_voff[n] = row * kbytes + 16 * lda_chunk[n];
   }
 #pragma unroll
   for (int n = 0; n < C::kLoadsB; ++n) {
-    const uint32_t row = kBN / 4 * wave + 16 * n + (lane >> 2);
+    const uint32_t row = kBN / kWaves * wave + 16 * n + (lane >> 2);
     ldb_chunk[n] = (lane & 3) ^ swz(row);
     ldb_voff[n] = row * kbytes + 16 * ldb_chunk[n];
   }
+  constexpr int kDmaPerStage = (kResid ? 2 : 1) * C::kLoadsA + C::kLoadsB;
+  constexpr int kMfmaPerStep = kTM * kTN * (kResid ? 2 : 1);
+  constexpr int kReadsPerStep = kTM * (kResid ? 2 : 1) + kTN;
+  constexpr int kScaleRowReads = kTM * (kResid ? 2 : 1) + kTN;
+  // scale pieces (64 rows x 16 B) per group: BM/64 for X and for R, BN/64
+  // for W, dealt round the waves; when they do not divide evenly the spare
+  // slots repeat pieces (identical bytes to the same place), so every wave
+  // issues as many loads
+  constexpr int kPiecesA = kBM / 64, kPiecesB = kBN / 64;
+  constexpr int kPieces = (kResid ? 2 : 1) * kPiecesA + kPiecesB;
+  constexpr int kScaleLoadsPerWave = (kPieces + kWaves - 1) / kWaves;
 
-  auto issue_stage = [&](int st, uint8_t* buf) {
+  // A stage past the end is still issued, at an out-of-range offset: it
+  // writes zeros into a slot nothing reads again, and keeps the number of
+  // loads per stage constant.
+  auto issue_stage = [&](int st) {
+    uint8_t* buf = ring + (st % kRing) * kStageBytes;
     const uint32_t kb = (uint32_t)st * kRowBytes;
+    const bool past_end = st >= nstages;
 #pragma unroll
     for (int n = 0; n < C::kLoadsA; ++n) {
       uint32_t vo = lda_voff[n] + kb;
-      if (!kFast && (uint32_t)st * (kBK / 32) + lda_chunk[n] >= kblocks) vo = kOOB;
-      uint8_t* dst = buf + (kBM / 4 * wave + 16 * n) * kRowBytes;
+      if ((!kFast && (uint32_t)st * (kBK / 32) + lda_chunk[n] >= kblocks) || past_end) vo = kOOB;
+      uint8_t* dst = buf + (kBM / kWaves * wave + 16 * n) * kRowBytes;
       load16_to_lds(rx, dst, vo);
       if (kResid) load16_to_lds(rr, dst + kTileBytesA, vo);
     }
 #pragma unroll
     for (int n = 0; n < C::kLoadsB; ++n) {
       uint32_t vo = ldb_voff[n] + kb;
-      if (!kFast && (uint32_t)st * (kBK / 32) + ldb_chunk[n] >= kblocks) vo = kOOB;
-      load16_to_lds(rw, buf + 2 * kTileBytesA + (kBN / 4 * wave + 16 * n) * kRowBytes, vo);
+      if ((!kFast && (uint32_t)st * (kBK / 32) + ldb_chunk[n] >= kblocks) || past_end) vo = kOOB;
+      load16_to_lds(rw, buf + 2 * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo);
     }
   };
 
-  // Scale loads for group g (stages 4g .. 4g + 3): 16 bytes per row, lane l
-  // of instruction j takes row 64 (j % 4) + l of operand j / 4 (X, R, W);
-  // wave w issues j = 3w, 3w + 1, 3w + 2.
-  auto issue_scale_rows = [&](__amdgpu_buffer_rsrc_t r, int g, uint8_t* dst, uint32_t row) {
-      if (kFast) {
-        load16_to_lds(r, dst, row * kblocks + 16 * g);
-      } else {
-        // gather byte by byte; blocks past K get a finite scale (their codes are zero)
-        uint32_t wv[4];
+  // Scale group g: 16 bytes (blocks 16 g .. 16 g + 15) of every row of X,
+  // R and W, as 64-row pieces.
+  auto issue_scale_piece = [&](__amdgpu_buffer_rsrc_t r, int g, int op, int q) {
+    const uint32_t row = 64 * q + lane;
+    uint8_t* dst = sbuf + op * kScaleBytesA + 64 * q * kScaleRowBytes;
+    if (kFast) {
+      load16_to_lds(r, dst, g < ngroups ? row * kblocks + 16 * g : kOOB);
+    } else {
+      // gather byte by byte; blocks past K get a finite scale (their codes are zero)
+      uint32_t wv[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint32_t v = 0;
+      for (int d = 0; d < 4; ++d) {
+        uint32_t v = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t blk = 16 * g + 4 * d + e;
-            const uint32_t b = blk < kblocks ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, row * kblocks + blk, 0, 0)
-                                             : 127u;
-            v |= b << (8 * e);
-          }
-          wv[d] = v;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t blk = 16 * g + 4 * d + e;
+          const uint32_t b =
+              blk < kblocks ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, row * kblocks + blk, 0, 0) : 127u;
+          v |= b << (8 * e);
         }
-        *reinterpret_cast<i32x4_t*>(dst + lane * kScaleRowBytes) =
-            i32x4_t{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+        wv[d] = v;
       }
+      *reinterpret_cast<i32x4_t*>(dst + lane * kScaleRowBytes) = i32x4_t{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+    }
   };
-  // Instruction j of a group covers 64 rows: j < A loads X rows, then R rows,
-  // then W rows (A = BM / 64); wave w issues j = w q .. w q + q - 1.
-  auto issue_scales = [&](int g, uint8_t* sbuf) {
-    constexpr int kA = C::kScaleLoadsA, kPerWave = C::kScaleLoads / 4;
+  auto issue_scales = [&](int g) {
 #pragma unroll
-    for (int q = 0; q < kPerWave; ++q) {
-      const int j = kPerWave * (int)wave + q;   // wave-uniform: plain branches, no descriptor select
-      if (j < kA) {
-        issue_scale_rows(rsx, g, sbuf + 64 * j * kScaleRowBytes, 64 * j + lane);
-      } else if (j < 2 * kA) {
-        if (kResid) issue_scale_rows(rsr, g, sbuf + kScaleBytesA + 64 * (j - kA) * kScaleRowBytes, 64 * (j - kA) + lane);
-      } else {
-        issue_scale_rows(rsw, g, sbuf + 2 * kScaleBytesA + 64 * (j - 2 * kA) * kScaleRowBytes, 64 * (j - 2 * kA) + lane);
-      }
+    for (int t = 0; t < kScaleLoadsPerWave; ++t) {
+      const int j = (kScaleLoadsPerWave * (int)wave + t) % kPieces;   // wave-uniform
+      if (j < kPiecesA)
+        issue_scale_piece(rsx, g, 0, j);
+      else if (kResid && j < 2 * kPiecesA)
+        issue_scale_piece(rsr, g, 1, j - kPiecesA);
+      else
+        issue_scale_piece(rsw, g, 2, j - (kResid ? 2 : 1) * kPiecesA);
     }
   };
 
-  // Per-lane LDS read offsets. A fragment of 32 rows starting at tile row
-  // 32 t: lane (lhalf, lrow) reads chunk (2 s + lhalf) of row 32 t + lrow.
-  uint32_t rd_off[kSteps];
+  // Per-lane LDS read offsets: lane (lhalf, lrow) of a 32-row fragment reads
+  // chunk 2 s + lhalf of its row.
+  uint32_t rd_off[2];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) rd_off[s] = lrow * kRowBytes + 16 * ((2 * s + lhalf) ^ swz(lrow));
-  const uint32_t a_row0 = kBM / kWavesM * wm, b_row0 = kBN / kWavesN * wn;
+  for (int s = 0; s < 2; ++s) rd_off[s] = lrow * kRowBytes + 16 * ((2 * s + lhalf) ^ swz(lrow));
+  const uint32_t a_row0 = kWaveM * wm, b_row0 = kWaveN * wn;
+
+  auto read_step = [&](int st, int s, i32x4_t (&ax)[kTM], i32x4_t (&ar)[kTM], i32x4_t (&bw)[kTN]) {
+    const uint8_t* buf = ring + (st % kRing) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const uint8_t* src = buf + (a_row0 + 32 * i) * kRowBytes + rd_off[s];
+      ax[i] = read_frag(src);
+      if (kResid) ar[i] = read_frag(src + kTileBytesA);
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) bw[j] = read_frag(buf + 2 * kTileBytesA + (b_row0 + 32 * j) * kRowBytes + rd_off[s]);
+  };
+  // this lane's scale words for two stages (a pair of the group's four)
+  i32x2_t gx[kTM], gr[kTM], gw[kTN];
+  auto read_scale_pair = [&](int pair) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const uint8_t* s0 = sbuf + (a_row0 + 32 * i + lrow) * kScaleRowBytes + 8 * pair;
+      gx[i] = *reinterpret_cast<const i32x2_t*>(s0);
+      if (kResid) gr[i] = *reinterpret_cast<const i32x2_t*>(s0 + kScaleBytesA);
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+      gw[j] = *reinterpret_cast<const i32x2_t*>(sbuf + 2 * kScaleBytesA + (b_row0 + 32 * j + lrow) * kScaleRowBytes + 8 * pair);
+  };
 
   f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -268,60 +366,92 @@ __global__ __launch_bounds__(kThreads, C::kOcc) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  const int nstages = (p.K + kBK - 1) / kBK;
-  i32x4_t gx[kTM], gr[kTM], gw[kTN];     // scale rows of the current group
-  issue_scales(0, scales);
-  issue_stage(0, tiles);
+  // Prologue: scales of group 0, then stages 0..2; wait for stage 0 (and the
+  // scales issued before it), make it visible, read its first step.
+  issue_scales(0);
+#pragma unroll
+  for (int st = 0; st < kRing; ++st) issue_stage(st);
+  if (kFast)
+    wait_vmcnt<2 * kDmaPerStage>();
+  else
+    wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  stage_barrier();
+  i32x4_t ax0[kTM], ar0[kTM], bw0[kTN], ax1[kTM], ar1[kTM], bw1[kTN];
+  read_scale_pair(0);
+  read_step(0, 0, ax0, ar0, bw0);
 
-  for (int st = 0; st < nstages; ++st) {
-    const uint8_t* buf = tiles + (st & 1) * kStageBytes;
-    const uint8_t* sbuf = scales + ((st / kScaleGroup) & 1) * kScaleBytes;
-    __builtin_amdgcn_s_waitcnt(0);      // this stage's tiles and scales have landed in LDS
-    __syncthreads();
-
-    i32x8_t ax[kSteps][kTM], ar[kSteps][kTM], bw[kSteps][kTN];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const uint8_t* src = buf + (a_row0 + 32 * i) * kRowBytes + rd_off[s];
-        ax[s][i] = read_frag(src);
-        if (kResid) ar[s][i] = read_frag(src + kTileBytesA);
-      }
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) bw[s][j] = read_frag(buf + 2 * kTileBytesA + (b_row0 + 32 * j) * kRowBytes + rd_off[s]);
-    }
-    // Scale words: every fourth stage each lane reads the 16 bytes (16
-    // blocks = 4 stages) of each of its rows in one ds_read_b128; word
-    // (st % 4) of them serves stage st, and byte 2 s of (word >> 8 lhalf) is
-    // the scale of block 4 st + 2 s + lhalf of the row.
-    if (st % kScaleGroup == 0) {
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const uint8_t* s0 = sbuf + (a_row0 + 32 * i + lrow) * kScaleRowBytes;
-        gx[i] = *reinterpret_cast<const i32x4_t*>(s0);
-        if (kResid) gr[i] = *reinterpret_cast<const i32x4_t*>(s0 + kScaleBytesA);
-      }
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        gw[j] = *reinterpret_cast<const i32x4_t*>(sbuf + 2 * kScaleBytesA + (b_row0 + 32 * j + lrow) * kScaleRowBytes);
-    }
-    const int sw_idx = st % kScaleGroup;
+  // One stage; P = st % 4 is a compile-time constant so that every wait count
+  // and scale-word index below is one.
+  auto stage = [&](auto pc, int st) {
+    constexpr int P = decltype(pc)::value;
+    __builtin_amdgcn_sched_barrier(0);   // keep each stage's schedule to itself
+    // scale words of this stage: byte 2 s of (word >> 8 lhalf) is block 4 st + 2 s + lhalf
+    // (the empty asm pins each extraction in its own stage, so the compiler
+    // does not compute all four stages' words up front and hold them)
     uint32_t cx[kTM], cr[kTM], cw[kTN];
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      cx[i] = (uint32_t)gx[i][sw_idx] >> (8 * lhalf);
-      cr[i] = kResid ? (uint32_t)gr[i][sw_idx] >> (8 * lhalf) : 0u;
+      cx[i] = (uint32_t)gx[i][P % 2];
+      asm volatile("" : "+v"(cx[i]));
+      cx[i] >>= 8 * lhalf;
+      if (kResid) {
+        cr[i] = (uint32_t)gr[i][P % 2];
+        asm volatile("" : "+v"(cr[i]));
+        cr[i] >>= 8 * lhalf;
+      } else {
+        cr[i] = 0u;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) cw[j] = (uint32_t)gw[j][sw_idx] >> (8 * lhalf);
-
-    if (st + 1 < nstages) {
-      if ((st + 1) % kScaleGroup == 0) issue_scales((st + 1) / kScaleGroup, scales + (((st + 1) / kScaleGroup) & 1) * kScaleBytes);
-      issue_stage(st + 1, tiles + ((st + 1) & 1) * kStageBytes);
+    for (int j = 0; j < kTN; ++j) {
+      cw[j] = (uint32_t)gw[j][P % 2];
+      asm volatile("" : "+v"(cw[j]));
+      cw[j] >>= 8 * lhalf;
     }
-    mfma_step<0, kResid, kTM, kTN>(acc, ax[0], ar[0], bw[0], cx, cr, cw);
-    mfma_step<1, kResid, kTM, kTN>(acc, ax[1], ar[1], bw[1], cx, cr, cw);
+
+    // first MFMA step; meanwhile read the second step's fragments
+    read_step(st, 1, ax1, ar1, bw1);
+    mfma_step<0, kResid, kTM, kTN>(acc, ax0, ar0, bw0, cx, cr, cw);
+    interleave_hint<kReadsPerStep, 0, kMfmaPerStep>();
+
+    // Stage st + 1 must have landed, and at the end of a group also the next
+    // group's scales. The only loads issued after those are stage st + 2's
+    // (scales go out before the stage loads of the same sync point, and
+    // every stage issues the same loads, see issue_stage).
+    if (kFast)
+      wait_vmcnt<kDmaPerStage>();
+    else
+      wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // every wave is past its reads of stage st: its slot takes stage st + 3;
+    // at P == 2 every wave also holds the group's last scale words, so the
+    // scale buffer takes the next group (issued first, see the wait above)
+    if (P == 2) issue_scales(st / kScaleGroup + 1);
+    issue_stage(st + kRing);
+
+    // second MFMA step; meanwhile read stage st + 1's first step and, after
+    // stages 1 and 3 of a group, the scale words of the next two stages (this
+    // stage's words were taken out of the registers above). Past the end
+    // these reads fetch values nobody uses.
+    if (P == 1) read_scale_pair(1);
+    if (P == 3) read_scale_pair(0);
+    read_step(st + 1, 0, ax0, ar0, bw0);
+    mfma_step<1, kResid, kTM, kTN>(acc, ax1, ar1, bw1, cx, cr, cw);
+    interleave_hint<kReadsPerStep + (P % 2 == 1 ? kScaleRowReads : 0),
+                    kFast ? kDmaPerStage + (P == 2 ? kScaleLoadsPerWave : 0) : 0, kMfmaPerStep>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // (the per-stage guards also keep each stage in its own block, which the
+  // register allocator needs to fit this loop without spills)
+  for (int st = 0; st < nstages; st += kScaleGroup) {
+    stage(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nstages) stage(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < nstages) stage(std::integral_constant<int, 2>{}, st + 2);
+    if (st + 3 < nstages) stage(std::integral_constant<int, 3>{}, st + 3);
   }
 
   // Epilogue: fp32 accumulators to Y.
@@ -350,22 +480,53 @@ __global__ __launch_bounds__(kThreads, C::kOcc) void gemm_kernel(GemmParams p) {
 }
 
 template <class C, bool kResid, bool kOutBf16>
-hipError_t launch_variant(GemmParams p, bool fast, hipStream_t stream) {
-  p.tiles_m = (p.M + C::kBM - 1) / C::kBM;
-  p.tiles_n = (p.N + C::kBN - 1) / C::kBN;
-  const int grid = p.tiles_m * p.tiles_n;
+hipError_t launch_tiles(const GemmParams& p, bool fast, hipStream_t stream) {
+  if (p.grid <= 0) return hipSuccess;
   if (fast)
-    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true>), dim3(p.grid), dim3(64 * C::kWaves), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, false>), dim3(p.grid), dim3(64 * C::kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
-template <class C>
-hipError_t launch_cfg(const GemmParams& p, bool resid, bool y_bf16, bool fast, hipStream_t stream) {
-  if (resid)
-    return y_bf16 ? launch_variant<C, true, true>(p, fast, stream) : launch_variant<C, true, false>(p, fast, stream);
-  return y_bf16 ? launch_variant<C, false, true>(p, fast, stream) : launch_variant<C, false, false>(p, fast, stream);
+// Plans the launch: big tiles, one workgroup per CU. When the tile count
+// leaves a last partial round that split into quadrants (two quadrant
+// workgroups per CU) finishes sooner, the whole rounds go out as big tiles
+// and the rest as quadrants in a second launch.
+template <bool kResid, bool kOutBf16>
+hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) {
+  p.gm = BigTile::kBM;
+  p.gn = BigTile::kBN;
+  p.tiles_m = (p.M + p.gm - 1) / p.gm;
+  p.tiles_n = (p.N + p.gn - 1) / p.gn;
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int rounds = tiles / cus, rest = tiles % cus;
+  // time in units of one big-tile round: a quadrant is a quarter of the work
+  // at half a CU, so a round of 2 * cus quadrants takes half a big round
+  const double all_big = rounds + (rest ? 1.0 : 0.0);
+  const double split = rounds + 0.5 * ((4 * rest + 2 * cus - 1) / (2 * cus));
+  const int big = (rest != 0 && split < all_big) ? rounds * cus : tiles;
+  p.first = 0;
+  p.grid = big;
+  p.quadrants = 0;
+  hipError_t e = launch_tiles<BigTile, kResid, kOutBf16>(p, fast, stream);
+  if (e != hipSuccess || big == tiles) return e;
+  p.first = big;
+  p.grid = 4 * (tiles - big);
+  p.quadrants = 1;
+  return launch_tiles<QuadTile, kResid, kOutBf16>(p, fast, stream);
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -378,7 +539,10 @@ hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, 
   p.y = y; p.ldy = ldy;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
   const bool fast = (K % (kBK * kScaleGroup)) == 0;
-  return launch_cfg<Tile128>(p, qr != nullptr, y_bf16, fast, stream);
+  const int cus = cu_count();
+  if (qr != nullptr)
+    return y_bf16 ? launch_variant<true, true>(p, fast, cus, stream) : launch_variant<true, false>(p, fast, cus, stream);
+  return y_bf16 ? launch_variant<false, true>(p, fast, cus, stream) : launch_variant<false, false>(p, fast, cus, stream);
 }
 
 }  // namespace rfq

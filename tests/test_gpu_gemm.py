@@ -179,6 +179,23 @@ def test_output_row_stride():
     check_y(yh[:, :N], y_ref, s_ref, torch.float32, "strided out")
 
 
+@pytest.mark.parametrize("M,N,K", [(4100, 4200, 1024), (4100, 4200, 640), (2304, 7000, 512)])
+def test_two_launch_split_sampled(M, N, K):
+    """Shapes whose 256 x 256 tile count leaves a partial last round: whole
+    rounds run as big tiles and the rest as quadrants, with partial edge
+    tiles in both; sampled rows x columns against the oracle (fp32 out)."""
+    rng = np.random.default_rng(M + N + K)
+    xb = heavy(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[gemm] two-launch split M={M} N={N} K={K}")
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    y = host(rfq.linear(dev_bf16(xb), wq, sw, out_dtype=torch.float32))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1, M - 4], rng.choice(M, 59, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, N - 1, N - 100], rng.choice(N, 57, replace=False)]))
+    y_ref, s_ref = oracle_y(xb[rows], wb[cols])
+    check_y(y[np.ix_(rows, cols)], y_ref, s_ref, torch.float32, f"split {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("name", ["qwen3vl_attn_proj", "qwen3vl_ffn_up", "wan22_ffn", "dit_ffn_down"])
 def test_full_size_config_sampled(name):
     """The configuration as the benchmark runs it (full X, full W, bf16 Y, one
