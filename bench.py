@@ -30,6 +30,7 @@ FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "RFQ W4A4 linear effective TFLOP/s (% MXFP4 peak); quantize GB/s (% HBM)"
 QUANT_BYTES_PER_ELEM = 2 + 2 * (0.5 + 1.0 / 32)      # bf16 in, Q(X) and Q(R) codes + scales out
+CPU_GEMM_ROWS = 4096                                  # rows of X in the oracle GEMM sample
 
 
 def parse():
@@ -69,9 +70,12 @@ def counter_traffic(workload, kernel_hash):
 
 
 def cpu_baseline(cfg):
-    """The oracle, as it stands, on a bounded sample of the workload; the
-    full-size time is extrapolated from per-row quantization time and
-    per-output GEMM time (labelled as such)."""
+    """The oracle, as it stands, on the workload: the residual quantization
+    of the whole X (one thread) and the K-doubled float64 GEMM on the first
+    CPU_GEMM_ROWS rows (all of them at the default size) against every
+    column of W (BLAS threads). With fewer rows the step time is the
+    quantize time plus the GEMM time scaled by M / CPU_GEMM_ROWS, labelled
+    as extrapolated."""
     import oracle
     import workloads
     try:
@@ -79,27 +83,31 @@ def cpu_baseline(cfg):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = os.cpu_count() or 1
-    q_rows, g_rows, g_cols = 512, 256, 2048
-    x = oracle.bf16_bits_to_f64(workloads.x_bf16(cfg, 0, q_rows))
-    w = oracle.bf16_bits_to_f64(workloads.w_bf16(cfg)[:g_cols])
+    g_rows = min(CPU_GEMM_ROWS, cfg.M)
+    x = oracle.bf16_bits_to_f64(workloads.x_bf16(cfg))
+    w = oracle.bf16_bits_to_f64(workloads.w_bf16(cfg))
     wq, sw = oracle.quantize_mxfp4(w)                      # setup, as on the GPU
+    del w
     t0 = time.perf_counter()
     qx, sx, qr, sr = oracle.residual_quantize(x)
     t_q = time.perf_counter() - t0
     t0 = time.perf_counter()
     oracle.gemm_w4a4(qx[:g_rows], sx[:g_rows], qr[:g_rows], sr[:g_rows], wq, sw)
     t_g = time.perf_counter() - t0
-    t_full = t_q / q_rows * cfg.M + t_g / (g_rows * g_cols) * cfg.M * cfg.N
+    t_full = t_q + t_g * cfg.M / g_rows
     value = 4.0 * cfg.M * cfg.N * cfg.K / t_full / 1e12
+    whole = g_rows == cfg.M
     return {
         "value": value,
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": (f"oracle residual_quantize on {q_rows} rows of X ({t_q:.2f} s, 1 thread) and oracle "
-                   f"K-doubled float64 GEMM on {g_rows} rows x {g_cols} columns ({t_g:.2f} s, "
-                   f"{blas_threads} BLAS threads); full {cfg.M}x{cfg.N}x{cfg.K} time extrapolated to "
-                   f"{t_full:.1f} s"),
+        "sample": (f"oracle residual_quantize on all {cfg.M} rows of X ({t_q:.2f} s, 1 thread) and oracle "
+                   f"K-doubled float64 GEMM (Y and its condition scale) on "
+                   + (f"all {cfg.M} x {cfg.N} outputs" if whole else f"rows 0..{g_rows - 1} x all {cfg.N} columns")
+                   + f" ({t_g:.2f} s, {blas_threads} BLAS threads): "
+                   + ("the whole step, " if whole else "full step extrapolated to ")
+                   + f"{t_full:.1f} s"),
     }
 
 
@@ -136,22 +144,26 @@ def main():
     stream = torch.cuda.current_stream()
     sp = rfq._stream()
 
-    def step(ev=None):
-        # the two launches of rfq_linear, with events between them
-        if ev is not None:
-            ev[0].record(stream)
+    def quantize():
         rfq._lib.check(lib.rfq_residual_quantize(x.data_ptr(), 0, M, K, x.stride(0), qx.data_ptr(), sx.data_ptr(),
                                                  qr.data_ptr(), sr.data_ptr(), sp))
-        if ev is not None:
-            ev[1].record(stream)
+
+    def gemm():
         rfq._lib.check(lib.rfq_gemm_w4a4(qx.data_ptr(), sx.data_ptr(), qr.data_ptr(), sr.data_ptr(), wq.data_ptr(),
                                          sw.data_ptr(), M, N, K, y.data_ptr(), rfq._lib.DTYPE_BF16, N, sp))
+
+    def step(ev=None):
+        # the two launches of rfq_linear; events around the GEMM call
+        quantize()
         if ev is not None:
-            ev[2].record(stream)
+            ev[0].record(stream)
+        gemm()
+        if ev is not None:
+            ev[1].record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -159,8 +171,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    gemm_times = np.array([e[0].elapsed_time(e[1]) for e in events])
+    gemm_ms = float(gemm_times.mean())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def batch_ms(fn, reps):
+        # back-to-back launches between two events: the per-launch time
+        # without an event between launches
+        for _ in range(3):
+            fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    quant_ms = batch_ms(quantize, 100)
 
     flops = 4.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -169,15 +196,7 @@ def main():
 
     # plain W4A4 GEMM (no residual operand) on the same operands, for the
     # overhead of the residual path
-    for _ in range(5):
-        rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out=y)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(50):
-        rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out=y)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    w4a4_ms = e0.elapsed_time(e1) / 50
+    w4a4_ms = batch_ms(lambda: rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out=y), 50)
 
     kernel_hash = source_hash("gemm.hip")
     traffic = counter_traffic(args.workload, kernel_hash)
@@ -210,6 +229,7 @@ def main():
             "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
             "traffic": traffic,
             "avg_launch_us": round(gemm_ms * 1e3, 2),
+            "median_launch_us": round(float(np.median(gemm_times)) * 1e3, 2),
         },
         "kernels": {
             "quantize_residual": {
@@ -217,6 +237,7 @@ def main():
                 "GB_per_s": round(quant_gbs, 1),
                 "pct_hbm_peak": round(100 * quant_gbs / HBM_PEAK_GBS, 2),
                 "algorithmic_bytes": QUANT_BYTES_PER_ELEM * M * K,
+                "note": "100 back-to-back launches; the 64 MB working set is partly served by the 256 MB last-level cache",
             },
             "gemm_rfq": {
                 "avg_launch_us": round(gemm_ms * 1e3, 2),
@@ -243,15 +264,7 @@ def main():
         def q5_step():
             rfq._lib.check(lib.rfq_residual_quantize(x5.data_ptr(), 0, c5.M, c5.K, c5.K, q5[0].data_ptr(),
                                                      s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
-        for _ in range(3):
-            q5_step()
-        e0.record(stream)
-        reps = 20
-        for _ in range(reps):
-            q5_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        q5_ms = e0.elapsed_time(e1) / reps
+        q5_ms = batch_ms(q5_step, 20)
         gbs = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5_ms * 1e-3) / 1e9
         out["kernels"]["quantize_residual_dit_ffn_down"] = {
             "shape": [c5.M, c5.K],

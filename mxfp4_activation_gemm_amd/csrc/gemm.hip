@@ -14,10 +14,13 @@
 // the E8M0 code of that (row, block) in the byte chosen by op_sel. Output
 // lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4.
 //
-// Tiling: a 256 x 256 output tile per workgroup of 4 waves on a 2 x 2 grid,
-// one wave per SIMD; each wave owns 128 x 128 outputs = 4 x 4 MFMA tiles
-// (256 fp32 accumulators per lane, in AGPRs). K advances 128 elements (64
-// bytes of codes per row) per stage, as two MFMA steps.
+// Tiling: a 256 x 256 output tile per workgroup of 8 waves on a 4 x 2 grid
+// (two waves per SIMD, one workgroup per CU); each wave owns 64 x 128
+// outputs = 2 x 4 MFMA tiles (128 fp32 accumulators per lane). K advances
+// 128 elements (64 bytes of codes per row) per stage, as two MFMA steps of
+// 64. When the tile count leaves a last partial round on the CUs, that
+// round's tiles are split into 128 x 128 quadrants run by 4-wave workgroups,
+// two per CU, in a second launch.
 //
 // Data movement:
 //  * Code tiles (QX, QR, W; 256 rows x 64 B each per stage) go global ->

@@ -53,7 +53,7 @@ def test_encoder_equals_brute_force_on_all_bf16_patterns():
         assert (got == brute_force_codes(x, se)).all(), se
 
 
-def test_encoder_equals_binadewise_bankers_rounding():
+def test_encoder_equals_per_binade_bankers_rounding():
     x = X_ALL[FINITE]
     for se in range(-3, 8):
         v = np.abs(np.ldexp(x, -se))
