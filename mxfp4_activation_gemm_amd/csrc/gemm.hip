@@ -12,7 +12,10 @@
 // and the 32 elements of K-block l / 32 of the 64-wide K step, as 16 bytes,
 // element 2j in the low nibble of byte j; its 32-bit scale operand supplies
 // the E8M0 code of that (row, block) in the byte chosen by op_sel. Output
-// lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4.
+// lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4. W is the
+// first operand and X (or R) the second, so an output tile is a tile of Y^T:
+// each lane holds one row of Y and, per group of four accumulators, four
+// consecutive columns, which leave as one vector store.
 //
 // Tiling: a 256 x 256 output tile per workgroup of 8 waves on a 4 x 2 grid
 // (two waves per SIMD, one workgroup per CU); each wave owns 64 x 128
@@ -33,6 +36,8 @@
 //    by choosing which chunk each lane fetches.
 //  * Stages live in a ring of three LDS buffers and are fetched two stages
 //    ahead, so a fetch that misses L2 has two stages of MFMA work to land.
+//    A stage's loads go out in two halves, one behind each MFMA step, so the
+//    memory pipeline gets an even stream rather than one burst per stage.
 //    Each wait names exactly the loads it needs (s_waitcnt vmcnt(N) with N =
 //    the loads issued after them), never "everything outstanding".
 //  * Scales: 16 bytes per row (16 blocks = 4 stages) per scale group, in one
@@ -46,6 +51,7 @@
 
 #include "kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace rfq {
@@ -54,6 +60,7 @@ namespace {
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -101,15 +108,29 @@ struct GemmParams {
   void* y;
   int64_t ldy;
   int32_t M, N, K;
-  // Tile map: `grid` workgroups; tiles of gm x gn form a tiles_m x tiles_n
-  // grid walked in a fixed logical order; workgroup ids map to logical tile
+  // Tile map: `grid` work items; tiles of gm x gn form a tiles_m x tiles_n
+  // grid walked in a fixed logical order; item ids map to logical tile
   // first + (0 .. grid - 1), or with `quadrants` to quadrant (id % 4) of
-  // logical tile first + id / 4.
+  // logical tile first + id / 4. The launch has `wg` workgroups; workgroup b
+  // runs items b, b + wg, b + 2 wg, ... back to back.
   int32_t tiles_m, tiles_n, gm, gn;
-  int32_t first, grid, quadrants;
+  int32_t first, grid, quadrants, wg;
+  int32_t vec_out;   // Y base and row stride allow 4-element vector stores
 };
 
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 2) & 3u; }
+
+// The kernel's parameter block, read again from the kernel-argument segment.
+// Code that runs once per tile uses it instead of values held since the
+// kernel started, so those do not occupy scalar registers through the loop.
+typedef __attribute__((address_space(4))) const GemmParams* const_params_ptr;
+__device__ __forceinline__ GemmParams fresh_params() {
+  const_params_ptr q = (const_params_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  GemmParams r;
+  __builtin_memcpy(&r, (const GemmParams*)q, sizeof(r));
+  return r;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // gfx9 raw buffer: stride 0, num_records in bytes, dword3 = 32-bit data format
@@ -175,15 +196,15 @@ __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x4
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ax[i]), widen(b[j]), acc[i][j], 4, 4, 2 * S,
-                                                                  (int)scx[i], 2 * S, (int)scw[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(b[j]), widen(ax[i]), acc[i][j], 4, 4, 2 * S,
+                                                                  (int)scw[j], 2 * S, (int)scx[i]);
   if (kResid) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ar[i]), widen(b[j]), acc[i][j], 4, 4, 2 * S,
-                                                                    (int)scr[i], 2 * S, (int)scw[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(b[j]), widen(ar[i]), acc[i][j], 4, 4, 2 * S,
+                                                                    (int)scw[j], 2 * S, (int)scr[i]);
   }
 }
 
@@ -208,8 +229,12 @@ __device__ __forceinline__ void interleave_hint() {
 
 // kFast: K % 512 == 0 (whole stages and whole 16-block scale groups); the
 // other instantiation masks partial K and waits for all loads at each stage.
-template <class C, bool kResid, bool kOutBf16, bool kFast>
+// kStream (needs kFast): every tile of the launch lies inside Y and Y takes
+// vector stores, and each workgroup streams several tiles; otherwise each
+// workgroup computes one tile and stores it with per-element bounds checks.
+template <class C, bool kResid, bool kOutBf16, bool kFast, bool kStream>
 __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParams p) {
+  static_assert(kFast || !kStream, "streaming needs whole scale groups");
   constexpr int kBM = C::kBM, kBN = C::kBN, kWaves = C::kWaves;
   constexpr int kWaveM = C::kWaveM, kWaveN = C::kWaveN, kTM = C::kTM, kTN = C::kTN;
   constexpr int kTileBytesA = C::kTileBytesA, kStageBytes = C::kStageBytes;
@@ -224,21 +249,33 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const unsigned wm = wave / kWavesN, wn = wave % kWavesN;
   const unsigned lrow = lane & 31, lhalf = lane >> 5;
-  int m0, n0;
-  tile_origin(p, blockIdx.x, m0, n0);
-  if (m0 >= p.M || n0 >= p.N) return;   // a quadrant past the edge (whole workgroup)
+  // This workgroup's items (tiles) run as one stream of K stages: while the
+  // last stages of one tile are computed, the first stages of the next are
+  // already being fetched, and the finished tile's stores drain behind the
+  // next tile's MFMAs. (Streaming needs whole scale groups per tile, kFast;
+  // otherwise the launch gives each workgroup one item.)
+  const int ntiles = (p.grid - (int)blockIdx.x + p.wg - 1) / p.wg;
+  int cm0, cn0;                                  // origin of the tile being computed
+  tile_origin(p, blockIdx.x, cm0, cn0);
+  if (cm0 >= p.M || cn0 >= p.N) return;          // a quadrant past the edge (whole workgroup)
   const uint32_t kbytes = (uint32_t)p.K / 2, kblocks = (uint32_t)p.K / 32;
-  const uint32_t rows_a = (uint32_t)min(kBM, p.M - m0), rows_b = (uint32_t)min(kBN, p.N - n0);
-
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.qx + (int64_t)m0 * kbytes, rows_a * kbytes);
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(kResid ? p.qr + (int64_t)m0 * kbytes : p.qx, rows_a * kbytes);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * kbytes, rows_b * kbytes);
-  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(p.sx + (int64_t)m0 * kblocks, rows_a * kblocks);
-  const __amdgpu_buffer_rsrc_t rsr = make_rsrc(kResid ? p.sr + (int64_t)m0 * kblocks : p.sx, rows_a * kblocks);
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
-
   const int nstages = (p.K + kBK - 1) / kBK;
   const int ngroups = (nstages + kScaleGroup - 1) / kScaleGroup;
+  const int total_stages = ntiles * nstages;
+
+  // Buffer descriptors of the tile being fetched (rows past the tensor read as zero).
+  __amdgpu_buffer_rsrc_t rx, rr, rw, rsx, rsr, rsw;
+  auto set_load_tile = [&](const GemmParams& q, int m0, int n0) {
+    const uint32_t rows_a = (uint32_t)min(kBM, q.M - m0), rows_b = (uint32_t)min(kBN, q.N - n0);
+    rx = make_rsrc(q.qx + (int64_t)m0 * kbytes, rows_a * kbytes);
+    rr = make_rsrc(kResid ? q.qr + (int64_t)m0 * kbytes : q.qx, rows_a * kbytes);
+    rw = make_rsrc(q.w + (int64_t)n0 * kbytes, rows_b * kbytes);
+    rsx = make_rsrc(q.sx + (int64_t)m0 * kblocks, rows_a * kblocks);
+    rsr = make_rsrc(kResid ? q.sr + (int64_t)m0 * kblocks : q.sx, rows_a * kblocks);
+    rsw = make_rsrc(q.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
+  };
+  set_load_tile(p, cm0, cn0);
+  int load_tile = 0, load_base = 0;              // tile being fetched and its first stream stage
 
   // Code-tile loads: wave w fetches rows [BM/waves w, BM/waves (w + 1)) of X
   // and R and the matching range of W's BN rows, 16 rows per instruction;
@@ -268,33 +305,44 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   constexpr int kPieces = (kResid ? 2 : 1) * kPiecesA + kPiecesB;
   constexpr int kScaleLoadsPerWave = (kPieces + kWaves - 1) / kWaves;
 
-  // A stage past the end is still issued, at an out-of-range offset: it
-  // writes zeros into a slot nothing reads again, and keeps the number of
-  // loads per stage constant.
-  auto issue_stage = [&](int st) {
+  // Stream stage st (stage st - load_base of the tile being fetched). A
+  // stage past the end of the stream is still issued, at an out-of-range
+  // offset: it writes zeros into a slot nothing reads again, and keeps the
+  // number of loads per stage constant. The loads go out in two parts.
+  constexpr int kPart0 = (kDmaPerStage + 1) / 2;
+  auto issue_stage = [&](int st, auto part_c) {
+    constexpr int part = decltype(part_c)::value;   // 0: first kPart0 loads, 1: the rest, 2: all
     uint8_t* buf = ring + (st % kRing) * kStageBytes;
-    const uint32_t kb = (uint32_t)st * kRowBytes;
-    const bool past_end = st >= nstages;
+    const int kst = st - load_base;
+    const uint32_t kb = (uint32_t)kst * kRowBytes;
+    const bool past_end = st >= total_stages;
 #pragma unroll
     for (int n = 0; n < C::kLoadsA; ++n) {
       uint32_t vo = lda_voff[n] + kb;
-      if ((!kFast && (uint32_t)st * (kBK / 32) + lda_chunk[n] >= kblocks) || past_end) vo = kOOB;
+      if ((!kFast && (uint32_t)kst * (kBK / 32) + lda_chunk[n] >= kblocks) || past_end) vo = kOOB;
       uint8_t* dst = buf + (kBM / kWaves * wave + 16 * n) * kRowBytes;
-      load16_to_lds(rx, dst, vo);
-      if (kResid) load16_to_lds(rr, dst + kTileBytesA, vo);
+      const int ix = (kResid ? 2 : 1) * n;
+      if (part == 2 || (ix < kPart0) == (part == 0)) load16_to_lds(rx, dst, vo);
+      if (kResid && (part == 2 || (ix + 1 < kPart0) == (part == 0))) load16_to_lds(rr, dst + kTileBytesA, vo);
     }
 #pragma unroll
     for (int n = 0; n < C::kLoadsB; ++n) {
       uint32_t vo = ldb_voff[n] + kb;
-      if ((!kFast && (uint32_t)st * (kBK / 32) + ldb_chunk[n] >= kblocks) || past_end) vo = kOOB;
-      load16_to_lds(rw, buf + 2 * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo);
+      if ((!kFast && (uint32_t)kst * (kBK / 32) + ldb_chunk[n] >= kblocks) || past_end) vo = kOOB;
+      const int ix = (kResid ? 2 : 1) * C::kLoadsA + n;
+      if (part == 2 || (ix < kPart0) == (part == 0))
+        load16_to_lds(rw, buf + 2 * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo);
     }
   };
 
-  // Scale group g: 16 bytes (blocks 16 g .. 16 g + 15) of every row of X,
-  // R and W, as 64-row pieces.
+  // Scale group g of the tile being fetched: 16 bytes (blocks 16 g .. 16 g +
+  // 15) of every row of X, R and W, as 64-row pieces.
   auto issue_scale_piece = [&](__amdgpu_buffer_rsrc_t r, int g, int op, int q) {
-    const uint32_t row = 64 * q + lane;
+    // (the lane index is re-read here so that the row offset is recomputed
+    // once per group instead of occupying a register through the loop)
+    uint32_t lane_now = lane;
+    asm volatile("" : "+v"(lane_now));
+    const uint32_t row = 64 * q + lane_now;
     uint8_t* dst = sbuf + op * kScaleBytesA + 64 * q * kScaleRowBytes;
     if (kFast) {
       load16_to_lds(r, dst, g < ngroups ? row * kblocks + 16 * g : kOOB);
@@ -316,7 +364,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       *reinterpret_cast<i32x4_t*>(dst + lane * kScaleRowBytes) = i32x4_t{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
     }
   };
-  auto issue_scales = [&](int g) {
+  auto issue_scales = [&](int stream_g) {
+    const int g = stream_g - load_base / kScaleGroup;   // past the stream end: g >= ngroups
 #pragma unroll
     for (int t = 0; t < kScaleLoadsPerWave; ++t) {
       const int j = (kScaleLoadsPerWave * (int)wave + t) % kPieces;   // wave-uniform
@@ -337,15 +386,21 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   const uint32_t a_row0 = kWaveM * wm, b_row0 = kWaveN * wn;
 
   auto read_step = [&](int st, int s, i32x4_t (&ax)[kTM], i32x4_t (&ar)[kTM], i32x4_t (&bw)[kTN]) {
-    const uint8_t* buf = ring + (st % kRing) * kStageBytes;
+    // one lane offset per step plus a scalar slot base; every fragment then
+    // sits at a constant distance from it (an instruction offset). (The lane
+    // offset is re-read here so that the compiler does not keep a separate
+    // precomputed address per ring slot and fragment through the loop.)
+    uint32_t off = rd_off[s];
+    asm volatile("" : "+v"(off));
+    const uint8_t* buf = ring + (st % kRing) * kStageBytes + off;
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const uint8_t* src = buf + (a_row0 + 32 * i) * kRowBytes + rd_off[s];
+      const uint8_t* src = buf + (a_row0 + 32 * i) * kRowBytes;
       ax[i] = read_frag(src);
       if (kResid) ar[i] = read_frag(src + kTileBytesA);
     }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) bw[j] = read_frag(buf + 2 * kTileBytesA + (b_row0 + 32 * j) * kRowBytes + rd_off[s]);
+    for (int j = 0; j < kTN; ++j) bw[j] = read_frag(buf + 2 * kTileBytesA + (b_row0 + 32 * j) * kRowBytes);
   };
   // this lane's scale words for two stages (a pair of the group's four)
   i32x2_t gx[kTM], gr[kTM], gw[kTN];
@@ -362,20 +417,24 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   };
 
   f32x16_t acc[kTM][kTN];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j)
+      for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  };
+  zero_acc();
 
   // Prologue: scales of group 0, then stages 0..2; wait for stage 0 (and the
   // scales issued before it), make it visible, read its first step.
   issue_scales(0);
 #pragma unroll
-  for (int st = 0; st < kRing; ++st) issue_stage(st);
+  for (int st = 0; st < kRing - 1; ++st) issue_stage(st, std::integral_constant<int, 2>{});
+  issue_stage(kRing - 1, std::integral_constant<int, 0>{});
   if (kFast)
-    wait_vmcnt<2 * kDmaPerStage>();
+    wait_vmcnt<kDmaPerStage + kPart0>();
   else
     wait_vmcnt<0>();
   wait_lgkmcnt0();
@@ -413,10 +472,12 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       cw[j] >>= 8 * lhalf;
     }
 
-    // first MFMA step; meanwhile read the second step's fragments
+    // first MFMA step; meanwhile read the second step's fragments and issue
+    // the second part of stage st + 2's loads
+    issue_stage(st + kRing - 1, std::integral_constant<int, 1>{});
     read_step(st, 1, ax1, ar1, bw1);
     mfma_step<0, kResid, kTM, kTN>(acc, ax0, ar0, bw0, cx, cr, cw);
-    interleave_hint<kReadsPerStep, 0, kMfmaPerStep>();
+    interleave_hint<kReadsPerStep, kFast ? kDmaPerStage - kPart0 : 0, kMfmaPerStep>();
 
     // Stage st + 1 must have landed, and at the end of a group also the next
     // group's scales. The only loads issued after those are stage st + 2's
@@ -432,8 +493,19 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     // every wave is past its reads of stage st: its slot takes stage st + 3;
     // at P == 2 every wave also holds the group's last scale words, so the
     // scale buffer takes the next group (issued first, see the wait above)
+    if (kStream && P == 1 && st + kRing - load_base == nstages && load_tile + 1 < ntiles) {
+      // the stream reaches the next tile with this stage's fetch (stage
+      // st + 3 = 4 g + 4, a tile start; every earlier fetch of the old tile
+      // has been issued, and none of the new one)
+      ++load_tile;
+      load_base += nstages;
+      const GemmParams q = fresh_params();
+      int m0, n0;
+      tile_origin(q, (int)blockIdx.x + load_tile * q.wg, m0, n0);
+      set_load_tile(q, m0, n0);
+    }
     if (P == 2) issue_scales(st / kScaleGroup + 1);
-    issue_stage(st + kRing);
+    issue_stage(st + kRing, std::integral_constant<int, 0>{});
 
     // second MFMA step; meanwhile read stage st + 1's first step and, after
     // stages 1 and 3 of a group, the scale words of the next two stages (this
@@ -444,51 +516,128 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     read_step(st + 1, 0, ax0, ar0, bw0);
     mfma_step<1, kResid, kTM, kTN>(acc, ax1, ar1, bw1, cx, cr, cw);
     interleave_hint<kReadsPerStep + (P % 2 == 1 ? kScaleRowReads : 0),
-                    kFast ? kDmaPerStage + (P == 2 ? kScaleLoadsPerWave : 0) : 0, kMfmaPerStep>();
+                    kFast ? kPart0 + (P == 2 ? kScaleLoadsPerWave : 0) : 0, kMfmaPerStep>();
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Epilogue of a tile: fp32 accumulators to Y. The weight is the MFMA's
+  // first operand, so tile (i, j) holds Y^T: lane (lhalf, lrow) has row m of
+  // Y and, in accumulator group q / 4, the four consecutive columns
+  // 8 (q / 4) + 4 lhalf + (0..3), stored together (8 bytes of bf16 or 16 of
+  // fp32) when the host found Y's base and row stride aligned for it.
+  auto store_tile = [&](int em0, int en0) {
+    const GemmParams q = fresh_params();
+    const int row_base = em0 + (int)a_row0 + (int)lrow;
+    const int col_base = en0 + (int)b_row0 + 4 * (int)lhalf;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int row = row_base + 32 * i;
+      if (row >= q.M) continue;
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = col_base + 32 * j + 8 * g;
+          const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          if (kOutBf16) {
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              uint32_t u = __builtin_bit_cast(uint32_t, v[e]);
+              u = (v[e] != v[e]) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u);
+              h[e] = (uint16_t)(u >> 16);
+            }
+            uint16_t* dst = reinterpret_cast<uint16_t*>(q.y) + (int64_t)row * q.ldy + col;
+            if (q.vec_out && col + 3 < q.N) {
+              *reinterpret_cast<i32x2_t*>(dst) = i32x2_t{(int)(h[0] | ((uint32_t)h[1] << 16)), (int)(h[2] | ((uint32_t)h[3] << 16))};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < q.N) dst[e] = h[e];
+            }
+          } else {
+            float* dst = reinterpret_cast<float*>(q.y) + (int64_t)row * q.ldy + col;
+            if (q.vec_out && col + 3 < q.N) {
+              *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < q.N) dst[e] = v[e];
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // The same for a tile that lies inside Y, with vector stores allowed. Each
+  // store is scheduled on its own (sched_barrier), so that only one group of
+  // converted values is live at a time: this runs inside the K loop, beside
+  // the next tile's fragments.
+  auto store_full_tile = [&](int em0, int en0) {
+    const GemmParams q = fresh_params();
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int64_t at = (int64_t)(em0 + (int)a_row0 + (int)lrow + 32 * i) * q.ldy + en0 + (int)b_row0 + 4 * (int)lhalf;
+      uint16_t* yb = reinterpret_cast<uint16_t*>(q.y) + at;
+      float* yf = reinterpret_cast<float*>(q.y) + at;
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& a = acc[i][j];
+          if (kOutBf16) {
+            uint32_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = a[4 * g + e];
+              const uint32_t u = __builtin_bit_cast(uint32_t, v);
+              h[e] = ((v != v) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+            }
+            *reinterpret_cast<i32x2_t*>(yb + 32 * j + 8 * g) = i32x2_t{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16))};
+          } else {
+            *reinterpret_cast<f32x4_t*>(yf + 32 * j + 8 * g) = f32x4_t{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
   };
 
   // (the per-stage guards also keep each stage in its own block, which the
   // register allocator needs to fit this loop without spills)
-  for (int st = 0; st < nstages; st += kScaleGroup) {
+  int comp_base = 0, comp_tile = 0;
+  for (int st = 0; st < total_stages; st += kScaleGroup) {
     stage(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < nstages) stage(std::integral_constant<int, 1>{}, st + 1);
-    if (st + 2 < nstages) stage(std::integral_constant<int, 2>{}, st + 2);
-    if (st + 3 < nstages) stage(std::integral_constant<int, 3>{}, st + 3);
-  }
-
-  // Epilogue: fp32 accumulators to Y.
-  const int row_base = m0 + (int)a_row0 + 4 * (int)lhalf;
-  const int col_base = n0 + (int)b_row0 + (int)lrow;
-#pragma unroll
-  for (int i = 0; i < kTM; ++i)
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int col = col_base + 32 * j;
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = row_base + 32 * i + 8 * (q / 4) + (q % 4);
-        if (row >= p.M) continue;
-        const float v = acc[i][j][q];
-        if (kOutBf16) {
-          uint32_t u = __builtin_bit_cast(uint32_t, v);
-          u = (v != v) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u);
-          reinterpret_cast<uint16_t*>(p.y)[(int64_t)row * p.ldy + col] = (uint16_t)(u >> 16);
-        } else {
-          reinterpret_cast<float*>(p.y)[(int64_t)row * p.ldy + col] = v;
-        }
-      }
+    if (st + 1 < total_stages) stage(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < total_stages) stage(std::integral_constant<int, 2>{}, st + 2);
+    if (st + 3 < total_stages) stage(std::integral_constant<int, 3>{}, st + 3);
+    if (kStream && st + kScaleGroup - comp_base == nstages && st + kScaleGroup < total_stages) {
+      // a tile ends here and another follows in the stream: store it, then
+      // start the next from zero (its first fragments are already read)
+      store_full_tile(cm0, cn0);
+      zero_acc();
+      ++comp_tile;
+      comp_base += nstages;
+      const GemmParams q = fresh_params();
+      tile_origin(q, (int)blockIdx.x + comp_tile * q.wg, cm0, cn0);
     }
+  }
+  if (kStream)
+    store_full_tile(cm0, cn0);
+  else
+    store_tile(cm0, cn0);
 }
 
-template <class C, bool kResid, bool kOutBf16>
-hipError_t launch_tiles(const GemmParams& p, bool fast, hipStream_t stream) {
+template <class C, bool kResid, bool kOutBf16, bool kCanStream>
+hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipStream_t stream) {
   if (p.grid <= 0) return hipSuccess;
-  if (fast)
-    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true>), dim3(p.grid), dim3(64 * C::kWaves), 0, stream, p);
+  if (kCanStream && stream_tiles)
+    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true, kCanStream>), dim3(p.wg), dim3(64 * C::kWaves), 0,
+                       stream, p);
+  else if (fast)
+    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, false>), dim3(p.grid), dim3(64 * C::kWaves), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, false, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -512,12 +661,18 @@ hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) 
   p.first = 0;
   p.grid = big;
   p.quadrants = 0;
-  hipError_t e = launch_tiles<BigTile, kResid, kOutBf16>(p, fast, stream);
+  // When every tile lies inside Y and Y takes vector stores, one workgroup
+  // per CU streams its tiles back to back; otherwise every tile gets its own
+  // workgroup.
+  const bool stream_tiles = fast && p.vec_out && p.M % BigTile::kBM == 0 && p.N % BigTile::kBN == 0 && big > cus;
+  p.wg = stream_tiles ? cus : big;
+  hipError_t e = launch_tiles<BigTile, kResid, kOutBf16, true>(p, fast, stream_tiles, stream);
   if (e != hipSuccess || big == tiles) return e;
   p.first = big;
   p.grid = 4 * (tiles - big);
   p.quadrants = 1;
-  return launch_tiles<QuadTile, kResid, kOutBf16>(p, fast, stream);
+  p.wg = p.grid;
+  return launch_tiles<QuadTile, kResid, kOutBf16, false>(p, fast, false, stream);
 }
 
 int cu_count() {
@@ -540,6 +695,9 @@ hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, 
   GemmParams p;
   p.qx = qx; p.sx = sx; p.qr = qr; p.sr = sr; p.w = w; p.sw = sw;
   p.y = y; p.ldy = ldy;
+  // four consecutive outputs go out as one 8-byte (bf16) or 16-byte (fp32) store
+  const uintptr_t vec_bytes = y_bf16 ? 8 : 16;
+  p.vec_out = ((uintptr_t)y % vec_bytes == 0 && ldy % 4 == 0) ? 1 : 0;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
   const bool fast = (K % (kBK * kScaleGroup)) == 0;
   const int cus = cu_count();

@@ -165,18 +165,24 @@ def test_linear_equals_quantize_then_gemm_bitwise_and_is_deterministic():
     assert (wsh[2 * c + s:2 * c + s + M * K // 32] == host(sr).ravel()).all()
 
 
-def test_output_row_stride():
+@pytest.mark.parametrize("out_dtype,ldy,offset", [(torch.float32, 96, 0), (torch.float32, 96, 1), (torch.float32, 98, 0),
+                                                  (torch.bfloat16, 96, 0), (torch.bfloat16, 96, 2),
+                                                  (torch.bfloat16, 97, 0)])
+def test_output_row_stride(out_dtype, ldy, offset):
+    """Y as a column slice of a wider buffer, at a row stride and base offset
+    that do or do not allow four-element vector stores; the columns around
+    the slice stay untouched."""
     rng = np.random.default_rng(24)
-    M, N, K = 40, 72, 192
+    M, N, K = 40, 73, 192
     xb, wb = heavy(rng, M, K), workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
     wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
-    big = torch.full((M, N + 24), 7.0, dtype=torch.float32, device="cuda")
-    log("[gemm] strided output")
-    rfq.linear(dev_bf16(xb), wq, sw, out=big[:, :N])
-    yh = host(big)
-    assert (yh[:, N:] == 7.0).all()
+    big = torch.full((M, ldy), 7.0, dtype=out_dtype, device="cuda")
+    log(f"[gemm] strided output {out_dtype} ldy={ldy} base offset {offset}")
+    rfq.linear(dev_bf16(xb), wq, sw, out=big[:, offset:offset + N])
+    yh = y_host(big)
+    assert (yh[:, :offset] == 7.0).all() and (yh[:, offset + N:] == 7.0).all()
     y_ref, s_ref = oracle_y(xb, wb)
-    check_y(yh[:, :N], y_ref, s_ref, torch.float32, "strided out")
+    check_y(yh[:, offset:offset + N], y_ref, s_ref, out_dtype, "strided out")
 
 
 @pytest.mark.parametrize("M,N,K", [(4100, 4200, 1024), (4100, 4200, 640), (2304, 7000, 512)])
@@ -194,6 +200,22 @@ def test_two_launch_split_sampled(M, N, K):
     cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, N - 1, N - 100], rng.choice(N, 57, replace=False)]))
     y_ref, s_ref = oracle_y(xb[rows], wb[cols])
     check_y(y[np.ix_(rows, cols)], y_ref, s_ref, torch.float32, f"split {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype", [(4096, 12288, 512, torch.float32), (4096, 8192, 1024, torch.bfloat16)])
+def test_streamed_tiles_every_output(M, N, K, out_dtype):
+    """M and N multiples of 256 with two or three whole rounds of tiles on
+    256 CUs: each workgroup computes its tiles back to back, fetching the
+    next tile's first stages while it finishes the previous one (with K =
+    512 every scale group starts a new tile). Every output checked."""
+    rng = np.random.default_rng(M + N + K + 7)
+    xb = heavy(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[gemm] streamed tiles M={M} N={N} K={K} {out_dtype}")
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    y = y_host(rfq.linear(dev_bf16(xb), wq, sw, out_dtype=out_dtype))
+    y_ref, s_ref = oracle_y(xb, wb)
+    check_y(y, y_ref, s_ref, out_dtype, f"streamed {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("name", ["qwen3vl_attn_proj", "qwen3vl_ffn_up", "wan22_ffn", "dit_ffn_down"])
