@@ -111,6 +111,39 @@ def cpu_baseline(cfg):
     }
 
 
+def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5):
+    """The power-limited ceiling of the GEMM's instruction on this workload's
+    own operand bytes: rfq_probe_mfma_ceiling runs only scaled FP4 MFMAs (no
+    memory traffic in the loop), one 8-wave workgroup per CU; the A operands
+    interleave Q(X) and Q(R) codes, the B operands are weight codes."""
+    lib = rfq.library()
+    props = torch.cuda.get_device_properties(0)
+    wgs = props.multi_processor_count
+    n = min(qx.numel(), qr.numel(), wq.numel(), 1 << 23) // 32 * 16
+    a = torch.stack([qx.view(-1)[:n].view(-1, 16), qr.view(-1)[:n].view(-1, 16)], 1).reshape(-1).contiguous()
+    b = wq.view(-1)[:2 * n].contiguous()
+    stamps = torch.zeros(2 * wgs, dtype=torch.int64, device=qx.device)
+    sink = torch.empty(512 * wgs, dtype=torch.float32, device=qx.device)
+    call = lambda: rfq._lib.check(lib.rfq_probe_mfma_ceiling(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), wgs,
+                                                             iters, stamps.data_ptr(), sink.data_ptr(), sp))
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * 32 * 32 * 64 * 32 * 8 * iters * wgs
+    st = stamps.cpu().numpy().reshape(-1, 2).astype(np.float64)
+    clock = float(np.median(st[:, 0] / (st[:, 1] * 10.0)))      # cycles per 100 MHz tick -> GHz
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"TFLOP_per_s": round(tf, 1), "pct_of_datasheet_peak": round(100 * tf / FP4_PEAK_TFLOPS, 2),
+            "shader_clock_GHz": round(clock, 3),
+            "what": "scaled FP4 MFMA loop on this workload's Q(X)/Q(R) and W codes, no memory traffic, "
+                    "one 8-wave workgroup per CU (rfq_probe_mfma_ceiling)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -198,6 +231,8 @@ def main():
     # overhead of the residual path
     w4a4_ms = batch_ms(lambda: rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out=y), 50)
 
+    ceiling = mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp)
+
     kernel_hash = source_hash("gemm.hip")
     traffic = counter_traffic(args.workload, kernel_hash)
     out = {
@@ -230,6 +265,7 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(gemm_ms * 1e3, 2),
             "median_launch_us": round(float(np.median(gemm_times)) * 1e3, 2),
+            "measured_mfma_ceiling": dict(ceiling, frac_of_ceiling=round(gemm_tflops / ceiling["TFLOP_per_s"], 4)),
         },
         "kernels": {
             "quantize_residual": {
@@ -266,13 +302,24 @@ def main():
                                                      s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
         q5_ms = batch_ms(q5_step, 20)
         gbs = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5_ms * 1e-3) / 1e9
+        del x5, q5, s5
+        # what a plain device-to-device copy reaches on this HBM (read + write)
+        ca = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cb = torch.empty_like(ca)
+        copy_ms = batch_ms(lambda: cb.copy_(ca), 10)
+        copy_gbs = 2.0 * ca.numel() / (copy_ms * 1e-3) / 1e9
+        del ca, cb
         out["kernels"]["quantize_residual_dit_ffn_down"] = {
             "shape": [c5.M, c5.K],
             "avg_launch_us": round(q5_ms * 1e3, 2),
             "GB_per_s": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "pct_of_device_copy": round(100 * gbs / copy_gbs, 2),
         }
-        del x5, q5, s5
+        out["kernels"]["hbm_device_copy_reference"] = {
+            "bytes_moved": 2 * (1 << 30), "GB_per_s": round(copy_gbs, 1),
+            "pct_hbm_peak": round(100 * copy_gbs / HBM_PEAK_GBS, 2),
+        }
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

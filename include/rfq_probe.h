@@ -1,0 +1,49 @@
+/*
+ * rfq_probe.h - measurement probe of librfq (not part of the RFQ layer).
+ *
+ * The FP4 GEMM on MI355X is limited by the chip's power budget before the
+ * MFMA issue rate: with real operand data the shader clock drops well below
+ * its 2.4 GHz peak. This probe measures that ceiling directly, as the rate of
+ * a loop that does nothing but issue the GEMM's instruction
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, both operands FP4) on operand bytes the
+ * caller supplies, with no memory traffic in the loop. The GEMM's throughput
+ * is then reported against both the datasheet peak and this ceiling.
+ */
+#ifndef RFQ_PROBE_H_
+#define RFQ_PROBE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rfq.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * rfq_probe_mfma_ceiling - launch `workgroups` workgroups of 512 threads
+ * (two waves per SIMD, as the GEMM runs; launch one per CU), each running
+ * `iters` iterations of 32 FP4 scaled MFMAs per wave over 8 independent
+ * accumulators. Each lane loads four 16-byte operands from each buffer once,
+ * before the loop, at consecutive 16-byte positions taken modulo the buffer
+ * size, so any buffer of at least 16 bytes serves.
+ *   a_codes, a_bytes: bytes of the first operand (e.g. Q(X) and Q(R) codes);
+ *   b_codes, b_bytes: bytes of the second operand (e.g. W codes); both
+ *     device pointers 16-byte aligned, sizes multiples of 16, at least 16;
+ *   stamps: device buffer of 2 * workgroups uint64 values (out): per
+ *     workgroup the shader-clock cycles and the 100 MHz constant-clock ticks
+ *     that its loop took;
+ *   sink: device buffer of 512 * workgroups floats (out): accumulator sums,
+ *     written so that the loop is not optimised away.
+ * Flops per call: 2 * 32 * 32 * 64 * 32 * 8 * iters * workgroups (8 waves of
+ * 32 MFMAs per iteration). Asynchronous on `stream`; errors as in rfq.h.
+ */
+rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
+                                    int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RFQ_PROBE_H_ */

@@ -32,6 +32,7 @@ SIGNATURES = {
     "rfq_status_string": (ctypes.c_char_p, [_i]),
     "rfq_last_error_detail": (ctypes.c_char_p, []),
     "rfq_abi_version": (_i, []),
+    "rfq_probe_mfma_ceiling": (_i, [_p, _sz, _p, _sz, _i, _i, _p, _p, _p]),
 }
 
 _LIB = None

@@ -9,6 +9,7 @@
 
 #include "kernels.h"
 #include "rfq.h"
+#include "rfq_probe.h"
 
 namespace {
 
@@ -184,5 +185,19 @@ const char* rfq_status_string(rfq_status_t status) {
 const char* rfq_last_error_detail(void) { return g_detail.c_str(); }
 
 int rfq_abi_version(void) { return RFQ_ABI_VERSION; }
+
+rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
+                                    int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream) {
+  if (a_codes == nullptr || b_codes == nullptr || stamps == nullptr || sink == nullptr)
+    return fail(RFQ_ERR_NULL_POINTER, "probe buffers must not be NULL");
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return fail(RFQ_ERR_MISALIGNED, "operands must be 16-byte aligned");
+  const size_t max_bytes = (size_t(1) << 32) * 16 - 16;
+  if (a_bytes < 16 || b_bytes < 16 || a_bytes % 16 || b_bytes % 16 || a_bytes > max_bytes || b_bytes > max_bytes)
+    return fail(RFQ_ERR_INVALID_SHAPE, "operand sizes must be multiples of 16 in [16, 2^36)");
+  if (workgroups <= 0 || workgroups > 65536 || iters <= 0)
+    return fail(RFQ_ERR_INVALID_SHAPE, "workgroups must be in [1, 65536] and iters positive");
+  return launched(rfq::launch_mfma_ceiling(a_codes, a_bytes, b_codes, b_bytes, workgroups, iters, stamps, sink,
+                                           static_cast<hipStream_t>(stream)));
+}
 
 }  // extern "C"

@@ -17,4 +17,8 @@ hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, 
                        const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N, int64_t K,
                        void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 
+// Measurement probe: the scaled FP4 MFMA loop on caller-supplied operands.
+hipError_t launch_mfma_ceiling(const uint8_t* a, size_t a_bytes, const uint8_t* b, size_t b_bytes, int workgroups,
+                               int iters, uint64_t* stamps, float* sink, hipStream_t stream);
+
 }  // namespace rfq

@@ -1,0 +1,66 @@
+// MFMA issue ceiling under the power limit (measurement probe, not part of
+// the RFQ layer): a loop of the GEMM's scaled FP4 MFMA on caller-supplied
+// operand bytes, with no memory traffic inside the loop, timed per
+// workgroup in shader-clock cycles (s_memtime) and in 100 MHz constant-clock
+// ticks (s_memrealtime), so that both the rate and the clock it ran at can be
+// read back.
+
+#include "kernels.h"
+
+namespace rfq {
+namespace {
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 512;   // two waves per SIMD, like the GEMM's main tile
+constexpr int kAcc = 8;         // independent accumulators per wave
+
+__global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a, uint32_t a_n, const i32x4_t* b,
+                                                                 uint32_t b_n, int iters, uint64_t* stamps,
+                                                                 float* sink) {
+  const uint32_t t = threadIdx.x;
+  i32x4_t ra[4], rb[4];
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t slot = (blockIdx.x * kThreads + t) * 4 + i;
+    ra[i] = a[slot % a_n];
+    rb[i] = b[slot % b_n];
+  }
+  f32x16_t acc[kAcc];
+  for (int q = 0; q < kAcc; ++q)
+    for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int q = 0; q < kAcc; ++q) {
+        const i32x4_t x = ra[(q + s) & 3], y = rb[(q / 2 + s) & 3];
+        acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(i32x8_t{x.x, x.y, x.z, x.w, 0, 0, 0, 0},
+                                                                 i32x8_t{y.x, y.y, y.z, y.w, 0, 0, 0, 0}, acc[q], 4, 4,
+                                                                 0, 120 + q, 0, 122);
+      }
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.f;
+  for (int q = 0; q < kAcc; ++q)
+    for (int e = 0; e < 16; ++e) sum += acc[q][e];
+  sink[blockIdx.x * kThreads + t] = sum;
+  if (t == 0) {
+    stamps[2 * blockIdx.x] = c1 - c0;
+    stamps[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_ceiling(const uint8_t* a, size_t a_bytes, const uint8_t* b, size_t b_bytes, int workgroups,
+                               int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(workgroups), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const i32x4_t*>(a), (uint32_t)(a_bytes / 16), reinterpret_cast<const i32x4_t*>(b),
+                     (uint32_t)(b_bytes / 16), iters, stamps, sink);
+  return hipGetLastError();
+}
+
+}  // namespace rfq

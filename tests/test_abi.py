@@ -1,5 +1,5 @@
 """The C ABI boundary without a GPU: the library loads, exports every entry
-point include/rfq.h declares, and rejects bad arguments on the host with the
+point include/*.h declares, and rejects bad arguments on the host with the
 documented status before anything is launched. Only calls that fail
 validation (or are zero-sized no-ops) are made here."""
 import os
@@ -9,7 +9,7 @@ import pytest
 
 from mxfp4_activation_gemm_amd import _lib
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "rfq.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 FAKE = 0x10000000          # a well-aligned non-null address; never dereferenced here
 
 
@@ -19,14 +19,17 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rfq_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(rfq_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declarations_are_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -111,3 +114,15 @@ def test_status_strings(lib):
     for code in range(1, 8):
         assert lib.rfq_status_string(code) not in (b"", b"unknown status")
     assert lib.rfq_status_string(99) == b"unknown status"
+
+
+def test_probe_validation(lib):
+    def pr(a=FAKE, an=4096, b=FAKE, bn=4096, wg=4, it=10, st=FAKE, sink=FAKE):
+        return status_name(lib.rfq_probe_mfma_ceiling(a, an, b, bn, wg, it, st, sink, None))
+    assert pr(a=None) == "RFQ_ERR_NULL_POINTER"
+    assert pr(sink=None) == "RFQ_ERR_NULL_POINTER"
+    assert pr(a=FAKE + 8) == "RFQ_ERR_MISALIGNED"
+    assert pr(an=8) == "RFQ_ERR_INVALID_SHAPE"
+    assert pr(bn=4100) == "RFQ_ERR_INVALID_SHAPE"
+    assert pr(wg=0) == "RFQ_ERR_INVALID_SHAPE"
+    assert pr(it=0) == "RFQ_ERR_INVALID_SHAPE"
