@@ -22,6 +22,9 @@ Sources followed (cited by page title and section):
   exponent with bias 1, 1-bit mantissa) rounded to nearest, ties to even,
   saturating at +-6.
 
+* The block-Hadamard rotation (``rotate.py``) follows the QuaRot description
+  on "大模型量化中的双线性尾部问题与QuaRot正交旋转解决方案" §3; see that module.
+
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against facts
 that do not come from this code (worked examples, closed forms, brute force,
 library routines, invariants). The one result without such a pin is the
@@ -48,6 +51,7 @@ from .quantize import (
     unpack_codes,
 )
 from .gemm import gemm_w4a4, linear
+from .rotate import hadamard32_f32, linear_rotated, rotate_quantize_weight, rotate_residual_quantize
 
 __all__ = [
     "BLOCK", "E2M1_EMAX", "E2M1_MAGNITUDES", "E8M0_NAN",
@@ -56,4 +60,5 @@ __all__ = [
     "scale_exponent", "encode_block_elements", "quantize_mxfp4", "residual_quantize",
     "dequantize", "pack_codes", "unpack_codes",
     "gemm_w4a4", "linear",
+    "hadamard32_f32", "rotate_residual_quantize", "rotate_quantize_weight", "linear_rotated",
 ]

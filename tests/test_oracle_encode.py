@@ -113,3 +113,28 @@ def test_scale_special_cases():
     se, code = oracle.scale_exponent(np.array([0.0, np.inf, np.nan, 2.0 ** -140]))
     assert list(code) == [0, 255, 255, 0]
     assert se[0] == -127 and se[3] == -127
+
+
+def test_encoder_on_float32_values_around_every_midpoint():
+    """float32 inputs carry 24 significant bits (the rotated path quantizes
+    them): values a few ulps either side of each E2M1 midpoint round to the
+    nearer neighbour, the midpoint itself to the even code, in every scale
+    window; checked against the brute-force rule and numpy's banker's rounding."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0], dtype=np.float32)
+    vals = [mids]
+    for k in range(1, 4):
+        vals.append(np.nextafter(mids, np.float32(np.inf)) if k == 1 else
+                    np.array([np.nextafter(np.nextafter(m, np.float32(np.inf)), np.float32(np.inf)) for m in mids],
+                             dtype=np.float32) if k == 2 else
+                    np.nextafter(mids, np.float32(0)))
+    v = np.concatenate(vals).astype(np.float32)
+    for se in (-10, -1, 0, 3, 50):
+        x = np.ldexp(v.astype(np.float64), se)
+        x = np.concatenate([x, -x])
+        assert (x.astype(np.float32).astype(np.float64) == x).all()
+        got = oracle.encode_block_elements(x, se)
+        assert (got == brute_force_codes(x, se)).all(), se
+        a = np.minimum(np.abs(np.ldexp(x, -se)), 6.0)
+        step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+        q = np.minimum(np.round(a / step) * step, 6.0)
+        assert (SPEC_E2M1[got & 7] == q).all(), se
