@@ -222,6 +222,11 @@ def main():
 
     quant_ms = batch_ms(quantize, 100)
 
+    def rotated_quantize():
+        rfq._lib.check(lib.rfq_rotate_residual_quantize(x.data_ptr(), 0, M, K, x.stride(0), qx.data_ptr(), sx.data_ptr(),
+                                                        qr.data_ptr(), sr.data_ptr(), sp))
+    rot_ms = batch_ms(rotated_quantize, 100)
+
     flops = 4.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -275,6 +280,12 @@ def main():
                 "algorithmic_bytes": QUANT_BYTES_PER_ELEM * M * K,
                 "note": "100 back-to-back launches; the 64 MB working set is partly served by the 256 MB last-level cache",
             },
+            "quantize_residual_rotated": {
+                "avg_launch_us": round(rot_ms * 1e3, 2),
+                "GB_per_s": round(QUANT_BYTES_PER_ELEM * M * K / (rot_ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * QUANT_BYTES_PER_ELEM * M * K / (rot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "what": "32-point block Hadamard of X fused before the RFQ pass (rfq_rotate_residual_quantize)",
+            },
             "gemm_rfq": {
                 "avg_launch_us": round(gemm_ms * 1e3, 2),
                 "TFLOP_per_s": round(gemm_tflops, 1),
@@ -302,6 +313,12 @@ def main():
                                                      s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
         q5_ms = batch_ms(q5_step, 20)
         gbs = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5_ms * 1e-3) / 1e9
+
+        def q5_rot():
+            rfq._lib.check(lib.rfq_rotate_residual_quantize(x5.data_ptr(), 0, c5.M, c5.K, c5.K, q5[0].data_ptr(),
+                                                            s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
+        q5r_ms = batch_ms(q5_rot, 20)
+        gbs_rot = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5r_ms * 1e-3) / 1e9
         del x5, q5, s5
         # what a plain device-to-device copy reaches on this HBM (read + write)
         ca = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -315,6 +332,12 @@ def main():
             "GB_per_s": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "pct_of_device_copy": round(100 * gbs / copy_gbs, 2),
+        }
+        out["kernels"]["quantize_residual_rotated_dit_ffn_down"] = {
+            "shape": [c5.M, c5.K],
+            "avg_launch_us": round(q5r_ms * 1e3, 2),
+            "GB_per_s": round(gbs_rot, 1),
+            "pct_hbm_peak": round(100 * gbs_rot / HBM_PEAK_GBS, 2),
         }
         out["kernels"]["hbm_device_copy_reference"] = {
             "bytes_moved": 2 * (1 << 30), "GB_per_s": round(copy_gbs, 1),

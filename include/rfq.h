@@ -22,7 +22,8 @@
  *     and so does its residual block.
  *
  * Data layout (all row-major, all DEVICE memory unless stated):
- *   - X: [rows, K] bfloat16, row stride ldx elements (ldx >= K);
+ *   - X: [rows, K] bfloat16 or float32 (x_dtype), row stride ldx elements
+ *     (ldx >= K);
  *   - codes: [rows, K/2] bytes, dense; byte j of a row holds element 2j in
  *     its low nibble and element 2j+1 in its high nibble;
  *   - scales: [rows, K/32] bytes, dense, one E8M0 code per block;
@@ -46,7 +47,8 @@
  *     K must be positive, a multiple of 32 and at most 2^22; rows, M and N
  *     below 2^31; rows * K, M * K and N * K below 2^37.
  *   - Alignment: X and every code pointer 16-byte aligned, and ldx a
- *     multiple of 8 elements (so every X row starts 16-byte aligned); Y
+ *     multiple of 8 elements for bf16 X or 4 for fp32 X (so every X row
+ *     starts 16-byte aligned); Y
  *     aligned to its element size; scale pointers need no alignment; the
  *     workspace 256-byte aligned.
  */
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RFQ_ABI_VERSION 1
+#define RFQ_ABI_VERSION 2
 
 typedef enum rfq_status {
   RFQ_OK = 0,
@@ -84,10 +86,10 @@ typedef void* rfq_stream_t;
 /*
  * rfq_quantize_mxfp4 - MXFP4 quantization of a bf16 matrix along K.
  * (The primary low-bit path of the pages' §1; also quantizes the weight.)
- *   x       [rows, K] bf16, stride ldx elements.       (in, device)
+ *   x       [rows, K] bf16 or fp32, stride ldx elements. (in, device)
  *   codes   [rows, K/2] bytes, dense.                  (out, device)
  *   scales  [rows, K/32] bytes, dense.                 (out, device)
- *   x_dtype must be RFQ_DTYPE_BF16.
+ *   x_dtype RFQ_DTYPE_BF16 or RFQ_DTYPE_FP32.
  */
 rfq_status_t rfq_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
                                 uint8_t* codes, uint8_t* scales, rfq_stream_t stream);
@@ -97,14 +99,42 @@ rfq_status_t rfq_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_
  * Q(X), then R = X - deq(Q(X)) exactly in fp32 (never rounded), then Q(R).
  * (The pages' §1: the full quantization error, with no threshold, rebuilt by a
  * second low-bit quantization path.)
- *   x        [M, K] bf16, stride ldx.                  (in, device)
+ *   x        [M, K] bf16 or fp32, stride ldx.          (in, device)
  *   qx_codes [M, K/2], qx_scales [M, K/32]: Q(X).      (out, device)
  *   qr_codes [M, K/2], qr_scales [M, K/32]: Q(R).      (out, device)
- *   x_dtype must be RFQ_DTYPE_BF16.
+ *   x_dtype RFQ_DTYPE_BF16 or RFQ_DTYPE_FP32.
+ * For fp32 X the residual is still exact in fp32: |R| is at most half an
+ * E2M1 step of the block scale, so X - deq(Q(X)) drops no bits.
  */
 rfq_status_t rfq_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                    uint8_t* qx_codes, uint8_t* qx_scales,
                                    uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream);
+
+/*
+ * Block-Hadamard rotation before quantization ("大模型量化中的双线性尾部问题与
+ * QuaRot正交旋转解决方案" §3, QuaRot: an orthogonal +-1 matrix applied online
+ * to the activation right before it is quantized and folded into the
+ * weight, so the layer's product is unchanged). H is the unnormalised
+ * 32 x 32 Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)),
+ * applied to every 32-element block along K, i.e. to every MX block; H H^T =
+ * 32 I, so with X H on the activation side and W H / 32 on the weight side
+ * rfq_gemm_w4a4 returns (X H)(W H / 32)^T = X W^T up to quantization.
+ * X H is formed in fp32 by five butterfly passes of spans 1, 2, 4, 8, 16,
+ * each taking (a, b) at block positions (i, i + span), i & span == 0, to
+ * (a + b, a - b); the codes are decided on those fp32 values.
+ *
+ * rfq_rotate_residual_quantize - the RFQ encoding of X H: Q(X H), then
+ *   R = X H - deq(Q(X H)) (exact in fp32), then Q(R). Arguments, layouts and
+ *   errors as rfq_residual_quantize.
+ * rfq_rotate_quantize_weight - MXFP4 codes and scales of W H / 32 (the 1/32,
+ *   a power of two, is exact). Arguments as rfq_quantize_mxfp4 (w [N, K],
+ *   stride ldw).
+ */
+rfq_status_t rfq_rotate_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                          uint8_t* qx_codes, uint8_t* qx_scales,
+                                          uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream);
+rfq_status_t rfq_rotate_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                        uint8_t* codes, uint8_t* scales, rfq_stream_t stream);
 
 /*
  * rfq_gemm_w4a4 - block-scaled FP4 GEMM, K-doubled for RFQ:
@@ -133,7 +163,7 @@ size_t rfq_linear_workspace_size(int64_t M, int64_t K);
 /*
  * rfq_linear - the whole RFQ W4A4 linear layer: rfq_residual_quantize into
  * the workspace, then rfq_gemm_w4a4, both on `stream`.
- *   x [M, K] bf16 stride ldx; w_codes/w_scales: W quantized by
+ *   x [M, K] bf16 or fp32 stride ldx; w_codes/w_scales: W quantized by
  *   rfq_quantize_mxfp4; y [M, N] fp32 or bf16 stride ldy;
  *   workspace: at least rfq_linear_workspace_size(M, K) bytes of device
  *   memory, 256-byte aligned, owned by the caller; its contents on return

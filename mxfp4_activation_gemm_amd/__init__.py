@@ -41,11 +41,12 @@ def _ptr(t):
 
 
 def _x_args(x):
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
-        raise ValueError("x must be a 2-D bfloat16 CUDA tensor")
+    """(rows, K, ldx, dtype code) of a 2-D bf16 or fp32 CUDA tensor with unit stride along K."""
+    if x.dtype not in (torch.bfloat16, torch.float32) or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 or float32 CUDA tensor")
     if x.stride(1) != 1:
         raise ValueError("x must have unit stride along K")
-    return x.shape[0], x.shape[1], x.stride(0)
+    return x.shape[0], x.shape[1], x.stride(0), (DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_FP32)
 
 
 def _y_dtype(out_dtype):
@@ -56,25 +57,42 @@ def _y_dtype(out_dtype):
     raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
 
 
-def quantize_mxfp4(x):
-    """MXFP4 along K: returns (codes uint8 [rows, K/2], scales uint8 [rows, K/32])."""
-    rows, K, ldx = _x_args(x)
+def _quantize(fn, x):
+    rows, K, ldx, dt = _x_args(x)
     codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
-    check(load().rfq_quantize_mxfp4(_ptr(x), DTYPE_BF16, rows, K, ldx, _ptr(codes), _ptr(scales), _stream()))
+    check(fn(_ptr(x), dt, rows, K, ldx, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
 
 
-def residual_quantize(x):
-    """RFQ encoding of X: returns (qx, sx, qr, sr) = Q(X) codes/scales, Q(R) codes/scales."""
-    M, K, ldx = _x_args(x)
+def _residual(fn, x):
+    M, K, ldx, dt = _x_args(x)
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     qr = torch.empty_like(qx)
     sx = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     sr = torch.empty_like(sx)
-    check(load().rfq_residual_quantize(_ptr(x), DTYPE_BF16, M, K, ldx, _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr),
-                                       _stream()))
+    check(fn(_ptr(x), dt, M, K, ldx, _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), _stream()))
     return qx, sx, qr, sr
+
+
+def quantize_mxfp4(x):
+    """MXFP4 along K of bf16 or fp32 X: returns (codes uint8 [rows, K/2], scales uint8 [rows, K/32])."""
+    return _quantize(load().rfq_quantize_mxfp4, x)
+
+
+def residual_quantize(x):
+    """RFQ encoding of X: returns (qx, sx, qr, sr) = Q(X) codes/scales, Q(R) codes/scales."""
+    return _residual(load().rfq_residual_quantize, x)
+
+
+def rotate_residual_quantize(x):
+    """RFQ encoding of X H (32-point block Hadamard along K): (qx, sx, qr, sr)."""
+    return _residual(load().rfq_rotate_residual_quantize, x)
+
+
+def rotate_quantize_weight(w):
+    """MXFP4 codes and scales of W H / 32, the weight side of the rotated layer."""
+    return _quantize(load().rfq_rotate_quantize_weight, w)
 
 
 def gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.bfloat16, out=None):
@@ -99,12 +117,12 @@ def linear_workspace_size(M, K):
 
 def linear(x, wq, sw, out_dtype=torch.bfloat16, out=None, workspace=None):
     """Whole RFQ W4A4 linear layer on bf16 X [M, K] and an MXFP4 weight."""
-    M, K, ldx = _x_args(x)
+    M, K, ldx, dt = _x_args(x)
     N = wq.shape[0]
     y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
     need = linear_workspace_size(M, K)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    check(load().rfq_linear(_ptr(x), DTYPE_BF16, M, K, ldx, _ptr(wq), _ptr(sw), N, _ptr(y), _y_dtype(y.dtype),
+    check(load().rfq_linear(_ptr(x), dt, M, K, ldx, _ptr(wq), _ptr(sw), N, _ptr(y), _y_dtype(y.dtype),
                             y.stride(0), _ptr(workspace), workspace.numel(), _stream()))
     return y

@@ -26,6 +26,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "rfq_quantize_mxfp4": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p]),
     "rfq_residual_quantize": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "rfq_rotate_residual_quantize": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "rfq_rotate_quantize_weight": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p]),
     "rfq_gemm_w4a4": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _i64, _p]),
     "rfq_linear_workspace_size": (_sz, [_i64, _i64]),
     "rfq_linear": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _i64, _p, _i, _i64, _p, _sz, _p]),

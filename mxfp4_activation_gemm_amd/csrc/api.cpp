@@ -46,10 +46,19 @@ rfq_status_t check_rows_k(int64_t rows, int64_t K, const char* rname) {
   return RFQ_OK;
 }
 
+rfq_status_t check_dtype(int x_dtype) {
+  if (x_dtype != RFQ_DTYPE_BF16 && x_dtype != RFQ_DTYPE_FP32)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: must be RFQ_DTYPE_BF16 or RFQ_DTYPE_FP32", x_dtype);
+  return RFQ_OK;
+}
+
+// X rows must start 16-byte aligned: ldx a multiple of 8 elements (bf16) or 4 (fp32).
 rfq_status_t check_x(const void* x, int x_dtype, int64_t K, int64_t ldx) {
-  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
-  if (ldx < K || ldx % 8 != 0)
-    return fail(RFQ_ERR_INVALID_STRIDE, "ldx = %lld must be >= K = %lld and a multiple of 8", (long long)ldx, (long long)K);
+  if (rfq_status_t st = check_dtype(x_dtype); st != RFQ_OK) return st;
+  const int64_t mult = x_dtype == RFQ_DTYPE_BF16 ? 8 : 4;
+  if (ldx < K || ldx % mult != 0)
+    return fail(RFQ_ERR_INVALID_STRIDE, "ldx = %lld must be >= K = %lld and a multiple of %lld", (long long)ldx,
+                (long long)K, (long long)mult);
   if (x == nullptr) return fail(RFQ_ERR_NULL_POINTER, "x is NULL");
   if (!aligned(x, 16)) return fail(RFQ_ERR_MISALIGNED, "x must be 16-byte aligned");
   return RFQ_OK;
@@ -85,30 +94,56 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 }  // namespace
 
+namespace {
+
+rfq_status_t quantize_common(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
+                             uint8_t* scales, int rotate, rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(rows, K, "rows"));
+  RFQ_TRY(check_dtype(x_dtype));
+  if (rows == 0) return ok();
+  RFQ_TRY(check_x(x, x_dtype, K, ldx));
+  RFQ_TRY(check_codes(codes, scales, "output"));
+  return launched(rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, rotate, rows, K, ldx, codes, scales, nullptr,
+                                       nullptr, static_cast<hipStream_t>(stream)));
+}
+
+rfq_status_t residual_common(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* qx_codes,
+                             uint8_t* qx_scales, uint8_t* qr_codes, uint8_t* qr_scales, int rotate,
+                             rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_dtype(x_dtype));
+  if (M == 0) return ok();
+  RFQ_TRY(check_x(x, x_dtype, K, ldx));
+  RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
+  RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
+  return launched(rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, rotate, M, K, ldx, qx_codes, qx_scales, qr_codes,
+                                       qr_scales, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 rfq_status_t rfq_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
                                 uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
-  RFQ_TRY(check_rows_k(rows, K, "rows"));
-  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
-  if (rows == 0) return ok();
-  RFQ_TRY(check_x(x, x_dtype, K, ldx));
-  RFQ_TRY(check_codes(codes, scales, "output"));
-  return launched(rfq::launch_quantize(static_cast<const uint16_t*>(x), rows, K, ldx, codes, scales, nullptr,
-                                       nullptr, static_cast<hipStream_t>(stream)));
+  return quantize_common(x, x_dtype, rows, K, ldx, codes, scales, 0, stream);
 }
 
 rfq_status_t rfq_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                    uint8_t* qx_codes, uint8_t* qx_scales,
                                    uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream) {
-  RFQ_TRY(check_rows_k(M, K, "M"));
-  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
-  if (M == 0) return ok();
-  RFQ_TRY(check_x(x, x_dtype, K, ldx));
-  RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
-  RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
-  return launched(rfq::launch_quantize(static_cast<const uint16_t*>(x), M, K, ldx, qx_codes, qx_scales, qr_codes,
-                                       qr_scales, static_cast<hipStream_t>(stream)));
+  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 0, stream);
+}
+
+rfq_status_t rfq_rotate_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                          uint8_t* qx_codes, uint8_t* qx_scales,
+                                          uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream) {
+  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 1, stream);
+}
+
+rfq_status_t rfq_rotate_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                        uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
+  return quantize_common(w, w_dtype, N, K, ldw, codes, scales, 2, stream);
 }
 
 rfq_status_t rfq_gemm_w4a4(const uint8_t* qx_codes, const uint8_t* qx_scales,
@@ -143,7 +178,7 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                         void* workspace, size_t workspace_bytes, rfq_stream_t stream) {
   RFQ_TRY(check_rows_k(M, K, "M"));
   RFQ_TRY(check_rows_k(N, K, "N"));
-  if (x_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: only RFQ_DTYPE_BF16 is accepted", x_dtype);
+  RFQ_TRY(check_dtype(x_dtype));
   if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
     return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
   if (M == 0 || N == 0) return ok();
@@ -163,7 +198,7 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
   uint8_t* qr = sx + scales;
   uint8_t* sr = qr + codes;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = rfq::launch_quantize(static_cast<const uint16_t*>(x), M, K, ldx, qx, sx, qr, sr, s);
+  hipError_t e = rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, 0, M, K, ldx, qx, sx, qr, sr, s);
   if (e != hipSuccess) return launched(e);
   return launched(rfq::launch_gemm(qx, sx, qr, sr, w_codes, w_scales, M, N, K, y, y_dtype == RFQ_DTYPE_BF16, ldy, s));
 }

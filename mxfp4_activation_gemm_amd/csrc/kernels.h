@@ -6,11 +6,12 @@
 
 namespace rfq {
 
-// MXFP4 quantization of a bf16 matrix along K, optionally with the RFQ
-// residual pass (qr/sr non-null). rows * (K/32) must be < 2^32.
-hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
-                           uint8_t* qx, uint8_t* sx, uint8_t* qr, uint8_t* sr,
-                           hipStream_t stream);
+// MXFP4 quantization of a bf16 (or, x_f32, fp32) matrix along K, optionally
+// with the RFQ residual pass (qr/sr non-null) and a block-Hadamard rotation
+// first (rotate 1: X H, with the residual pass; rotate 2: X H / 32, without).
+// rows * (K/32) must be < 2^32.
+hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int64_t rows, int64_t K, int64_t ldx,
+                           uint8_t* qx, uint8_t* sx, uint8_t* qr, uint8_t* sr, hipStream_t stream);
 
 // Block-scaled FP4 GEMM, Y = QX.W^T (+ QR.W^T when qr != nullptr).
 hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, const uint8_t* sr,

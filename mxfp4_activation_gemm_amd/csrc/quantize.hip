@@ -20,6 +20,19 @@
 // on the way back. The residual never leaves fp32 registers.
 //
 // Traffic per element: 2 B read, 2 x (0.5 + 1/32) B written = 3.0625 B.
+//
+// Variants of the same pass:
+//  * fp32 input (8 values = 32 bytes per lane);
+//  * rotation before quantization ("大模型量化中的双线性尾部问题与QuaRot正交旋转
+//    解决方案" §3, QuaRot: an orthogonal +-1 matrix applied online to the
+//    activation and folded into the weight): each 32-block is multiplied by
+//    the unnormalised 32 x 32 Sylvester Hadamard matrix H in fp32, by five
+//    butterfly passes of spans 1, 2, 4 (inside a lane) and 8, 16 (across the
+//    block's four lanes, DPP), each taking (a, b) at (i, i + span) to
+//    (a + b, a - b). Activations quantize X H; weights W H / 32 (an exact
+//    power of two), so the GEMM returns X W^T unchanged. Codes are decided
+//    on the rotated fp32 values; the residual stays exact (|R| is at most
+//    half an E2M1 step, so R = v - deq(v) loses no bits in fp32).
 
 #include "kernels.h"
 
@@ -27,6 +40,7 @@ namespace rfq {
 namespace {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -93,8 +107,48 @@ __device__ __forceinline__ void residual_pair(const float* x, unsigned codes, fl
   r[2 * J + 1] = x[2 * J + 1] - d.y;
 }
 
+// One butterfly pass across lanes: this lane's element pairs with the same
+// element of lane (lane ^ kXor) in its quad; the lane with the span bit clear
+// keeps a + b, the other a - b (a = the clear lane's value).
+// (o - a is formed as (-a) + o: negation is exact, so the result is the same
+// IEEE sum, and the partner's value can feed the add through DPP directly.)
+template <int kDpp>
+__device__ __forceinline__ void butterfly_across(float* v, bool upper) {
+  const unsigned flip = upper ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float o = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[j]), kDpp, 0xF, 0xF, true));
+    v[j] = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, v[j]) ^ flip) + o;
+  }
+}
+
+// Walsh-Hadamard transform of the 32-block held by a quad of lanes (lane part
+// p holds elements 8 p .. 8 p + 7), unnormalised, in the pass order above.
+__device__ __forceinline__ void hadamard32(float* v, unsigned part) {
+#pragma unroll
+  for (int span = 1; span < 8; span *= 2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (!(j & span)) {
+        const float a = v[j], b = v[j + span];
+        v[j] = a + b;
+        v[j + span] = a - b;
+      }
+  butterfly_across<kQuadXor1>(v, part & 1);   // span 8
+  butterfly_across<kQuadXor2>(v, part & 2);   // span 16
+}
+
+// max over 8 fp32 magnitudes as a bit pattern (monotone in the value for
+// non-NaN inputs; >= 0x7F800000 means Inf or NaN)
+__device__ __forceinline__ unsigned f32x8_absmax_bits(const float* v) {
+  unsigned m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = max(m, __builtin_bit_cast(unsigned, v[j]) & 0x7FFFFFFFu);
+  return m;
+}
+
 struct QuantParams {
-  const uint16_t* x;
+  const void* x;
   int64_t ldx;            // elements
   uint8_t* qx;
   uint8_t* sx;
@@ -104,7 +158,9 @@ struct QuantParams {
   uint32_t total_blocks;  // rows * K / 32
 };
 
-template <bool kResidual>
+// kF32In: X is fp32 (else bf16). kRotate: 0 none, 1 X H (activations),
+// 2 X H / 32 (weights).
+template <bool kResidual, bool kF32In, int kRotate>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const unsigned lane = threadIdx.x & 63;
   const unsigned wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -116,7 +172,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   uint32_t row0 = g0 / p.nblk_row;
   uint32_t col0 = g0 - row0 * p.nblk_row;
 
-  u32x4_t w[kUnits];
+  // the lane's 8 values of each unit: one 16-byte load of bf16, or two of fp32
+  constexpr int kLoads = kF32In ? 2 : 1;
+  u32x4_t w[kUnits][kLoads];
   uint32_t gblk[kUnits];
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
@@ -124,21 +182,45 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     uint32_t b = col0 + u * 16 + quad, r = row0;
     while (b >= p.nblk_row) { b -= p.nblk_row; ++r; }
     gblk[u] = g;
-    const uint16_t* src = p.x + (int64_t)r * p.ldx + (int64_t)b * 32 + part * 8;
-    w[u] = (g < p.total_blocks) ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0, 0, 0, 0};
+    const int64_t elem = (int64_t)r * p.ldx + (int64_t)b * 32 + part * 8;
+    const u32x4_t* src = kF32In ? reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + elem)
+                                : reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + elem);
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) w[u][h] = (g < p.total_blocks) ? src[h] : u32x4_t{0, 0, 0, 0};
   }
 
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
     const uint32_t g = gblk[u];
     const bool valid = g < p.total_blocks;
-    const unsigned amax = quad_max_u32(bf16x8_absmax_bits(w[u]));
-    const unsigned e = amax >> 7;                      // bf16 biased exponent of amax
+    float xf[8];
+    unsigned e;                                        // biased exponent of the block amax (fp32/bf16 field)
+    if (!kF32In && kRotate == 0) {
+      const unsigned amax = quad_max_u32(bf16x8_absmax_bits(w[u][0]));
+      e = amax >> 7;
+      widen_bf16x8(w[u][0], xf);
+    } else {
+      if (kF32In) {
+        // (whole-vector bit casts: a bit cast of a single ext-vector element
+        // has been seen to read element 0)
+        const f32x4_t lo = __builtin_bit_cast(f32x4_t, w[u][0]), hi = __builtin_bit_cast(f32x4_t, w[u][kLoads - 1]);
+        xf[0] = lo.x; xf[1] = lo.y; xf[2] = lo.z; xf[3] = lo.w;
+        xf[4] = hi.x; xf[5] = hi.y; xf[6] = hi.z; xf[7] = hi.w;
+      } else {
+        widen_bf16x8(w[u][0], xf);
+      }
+      if (kRotate != 0) {
+        hadamard32(xf, part);
+        if (kRotate == 2) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xf[j] *= 0.03125f;   // 1/32, exact
+        }
+      }
+      e = quad_max_u32(f32x8_absmax_bits(xf)) >> 23;
+    }
     const bool nonfinite = e == 255;
     const unsigned sxc = nonfinite ? 255u : (e > 2 ? e - 2 : 0u);
     const float s = scale_operand(sxc);
-    float xf[8];
-    widen_bf16x8(w[u], xf);
     unsigned cx = encode_f32x8(xf, s);
     if (nonfinite) cx = 0;
 
@@ -175,9 +257,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 
 }  // namespace
 
-hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
-                           uint8_t* qx, uint8_t* sx, uint8_t* qr, uint8_t* sr,
-                           hipStream_t stream) {
+hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int64_t rows, int64_t K, int64_t ldx,
+                           uint8_t* qx, uint8_t* sx, uint8_t* qr, uint8_t* sr, hipStream_t stream) {
   QuantParams p;
   p.x = x;
   p.ldx = ldx;
@@ -189,10 +270,26 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t l
   p.total_blocks = (uint32_t)(rows * (K / 32));
   const uint64_t waves = (p.total_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
   const uint64_t groups = (waves + kThreads / 64 - 1) / (kThreads / 64);
-  if (qr != nullptr)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)groups), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)groups), dim3(kThreads), 0, stream, p);
+  const dim3 grid((unsigned)groups), block(kThreads);
+  const bool resid = qr != nullptr;
+  // rotate 1 goes with the residual pass (activations), rotate 2 without it (weights)
+  if (rotate == 1 && resid) {
+    if (x_f32) hipLaunchKernelGGL((quantize_kernel<true, true, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((quantize_kernel<true, false, 1>), grid, block, 0, stream, p);
+  } else if (rotate == 2 && !resid) {
+    if (x_f32) hipLaunchKernelGGL((quantize_kernel<false, true, 2>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((quantize_kernel<false, false, 2>), grid, block, 0, stream, p);
+  } else if (rotate == 0) {
+    if (resid) {
+      if (x_f32) hipLaunchKernelGGL((quantize_kernel<true, true, 0>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((quantize_kernel<true, false, 0>), grid, block, 0, stream, p);
+    } else {
+      if (x_f32) hipLaunchKernelGGL((quantize_kernel<false, true, 0>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((quantize_kernel<false, false, 0>), grid, block, 0, stream, p);
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -12,6 +12,13 @@ from mxfp4_activation_gemm_amd import _lib
 INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 FAKE = 0x10000000          # a well-aligned non-null address; never dereferenced here
 
+# These calls pass fake device addresses that validation must reject before
+# any launch; where a GPU is visible a validation slip would launch a kernel on
+# them, so the module runs only on GPU-less hosts (the GPU tests cover the
+# same entry points with real buffers).
+pytestmark = pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                                reason="fake-pointer validation checks run on hosts without a GPU")
+
 
 @pytest.fixture(scope="module")
 def lib():
@@ -29,11 +36,11 @@ def declared_functions():
 
 def test_header_declarations_are_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
-    assert lib.rfq_abi_version() == 1
+    assert lib.rfq_abi_version() == 2
 
 
 def status_name(st):
@@ -54,9 +61,11 @@ def test_quantize_validation(lib):
     assert q(lib, rows=-1) == "RFQ_ERR_INVALID_SHAPE"
     assert q(lib, rows=1 << 31) == "RFQ_ERR_INVALID_SHAPE"
     assert q(lib, rows=1 << 22, K=1 << 15, ldx=1 << 15) == "RFQ_ERR_INVALID_SHAPE"   # 2^37 elements
-    assert q(lib, dt=1) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert q(lib, dt=2) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert q(lib, dt=-1) == "RFQ_ERR_UNSUPPORTED_DTYPE"
     assert q(lib, ldx=32) == "RFQ_ERR_INVALID_STRIDE"
-    assert q(lib, ldx=68) == "RFQ_ERR_INVALID_STRIDE"
+    assert q(lib, ldx=68) == "RFQ_ERR_INVALID_STRIDE"              # bf16 rows need a multiple of 8
+    assert q(lib, dt=1, ldx=66) == "RFQ_ERR_INVALID_STRIDE"        # fp32 rows need a multiple of 4
     assert q(lib, x=FAKE + 8) == "RFQ_ERR_MISALIGNED"
     assert q(lib, codes=FAKE + 4) == "RFQ_ERR_MISALIGNED"
     assert q(lib, x=None, rows=0) == "RFQ_OK"              # empty input: no-op, pointers unused
@@ -104,8 +113,10 @@ def test_linear_workspace_rule_and_validation(lib):
     assert status_name(f(FAKE, 0, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, None, need, None)) == "RFQ_ERR_NULL_POINTER"
     assert status_name(f(FAKE, 0, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, FAKE + 16, need, None)) == \
         "RFQ_ERR_MISALIGNED"
-    assert status_name(f(FAKE, 1, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, FAKE, need, None)) == \
+    assert status_name(f(FAKE, 5, 8, 64, 64, FAKE, FAKE, 8, FAKE, 0, 8, FAKE, need, None)) == \
         "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert status_name(f(FAKE, 1, 8, 64, 62, FAKE, FAKE, 8, FAKE, 0, 8, FAKE, need, None)) == \
+        "RFQ_ERR_INVALID_STRIDE"                                   # fp32 X, row stride not a multiple of 4
     assert status_name(f(None, 0, 0, 64, 64, None, None, 8, None, 0, 8, None, 0, None)) == "RFQ_OK"
 
 
@@ -126,3 +137,15 @@ def test_probe_validation(lib):
     assert pr(bn=4100) == "RFQ_ERR_INVALID_SHAPE"
     assert pr(wg=0) == "RFQ_ERR_INVALID_SHAPE"
     assert pr(it=0) == "RFQ_ERR_INVALID_SHAPE"
+
+
+def test_rotated_quantize_validation(lib):
+    f, w = lib.rfq_rotate_residual_quantize, lib.rfq_rotate_quantize_weight
+    assert status_name(f(FAKE, 0, 4, 64, 64, FAKE, FAKE, None, FAKE, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(f(FAKE, 3, 4, 64, 64, FAKE, FAKE, FAKE, FAKE, None)) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert status_name(f(FAKE, 0, 4, 48, 48, FAKE, FAKE, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_SHAPE"
+    assert status_name(f(None, 0, 0, 64, 64, None, None, None, None, None)) == "RFQ_OK"
+    assert status_name(w(FAKE, 1, 4, 64, 62, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_STRIDE"
+    assert status_name(w(FAKE + 4, 1, 4, 64, 64, FAKE, FAKE, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(w(FAKE, 0, 4, 64, 64, None, FAKE, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(w(None, 0, 0, 64, 64, None, None, None)) == "RFQ_OK"
