@@ -24,6 +24,9 @@ Sources followed (cited by page title and section):
 
 * The block-Hadamard rotation (``rotate.py``) follows the QuaRot description
   on "大模型量化中的双线性尾部问题与QuaRot正交旋转解决方案" §3; see that module.
+* MXFP8 (``mxfp8.py``): E4M3 elements per OCP MX v1.0, for the W4A8 layer and
+  for RFQ with an MXFP8 residual path (the pages study MXFP8 beside MXFP4,
+  Abstract and §1); see that module.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against facts
 that do not come from this code (worked examples, closed forms, brute force,
@@ -52,6 +55,20 @@ from .quantize import (
 )
 from .gemm import gemm_w4a4, linear
 from .rotate import hadamard32_f32, linear_rotated, rotate_quantize_weight, rotate_residual_quantize
+from .mxfp8 import (
+    E4M3_MAGNITUDES,
+    E4M3_MAX,
+    dequantize_mxfp8,
+    e4m3_value,
+    encode_e4m3,
+    gemm_w4a4_fp8_residual,
+    gemm_w4a8,
+    linear_fp8_residual,
+    linear_w4a8,
+    quantize_mxfp8,
+    residual_quantize_fp8,
+    scale_exponent_e4m3,
+)
 
 __all__ = [
     "BLOCK", "E2M1_EMAX", "E2M1_MAGNITUDES", "E8M0_NAN",
@@ -61,4 +78,7 @@ __all__ = [
     "dequantize", "pack_codes", "unpack_codes",
     "gemm_w4a4", "linear",
     "hadamard32_f32", "rotate_residual_quantize", "rotate_quantize_weight", "linear_rotated",
+    "E4M3_MAGNITUDES", "E4M3_MAX", "e4m3_value", "scale_exponent_e4m3", "encode_e4m3",
+    "quantize_mxfp8", "dequantize_mxfp8", "residual_quantize_fp8",
+    "gemm_w4a8", "gemm_w4a4_fp8_residual", "linear_w4a8", "linear_fp8_residual",
 ]
