@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RFQ_ABI_VERSION 2
+#define RFQ_ABI_VERSION 3
 
 typedef enum rfq_status {
   RFQ_OK = 0,
@@ -154,6 +154,56 @@ rfq_status_t rfq_gemm_w4a4(const uint8_t* qx_codes, const uint8_t* qx_scales,
                            const uint8_t* w_codes, const uint8_t* w_scales,
                            int64_t M, int64_t N, int64_t K,
                            void* y, int y_dtype, int64_t ldy, rfq_stream_t stream);
+
+/*
+ * MXFP8 variants. The pages ("Activation Outliers Matter", Abstract and §1)
+ * study MXFP8 beside MXFP4 and find it close to lossless; they name it
+ * without defining it. This library follows OCP MX v1.0 MXFP8 with E4M3
+ * elements:
+ *   - element: E4M3 code, bit 7 sign, 4 exponent bits (bias 7), 3 mantissa
+ *     bits, subnormals at exponent 0, S.1111.111 is NaN, no infinities;
+ *     largest normal 448;
+ *   - shared scale: E8M0 as above with se = max(floor(log2(amax)) - 8, -127);
+ *   - x / 2^se is rounded to nearest, ties to even, saturating at +-448; the
+ *     sign bit of x is kept; a block holding NaN or +-Inf gets scale 255 and
+ *     codes 0;
+ *   - layout: codes [rows, K] bytes, dense, byte k = element k; scales
+ *     [rows, K/32] as for MXFP4.
+ * The weight stays MXFP4 (rfq_quantize_mxfp4) in both GEMM variants.
+ *
+ * rfq_quantize_mxfp8 - MXFP8 quantization of a bf16 or fp32 matrix along K.
+ *   Arguments as rfq_quantize_mxfp4; codes [rows, K] bytes (out, device).
+ *
+ * rfq_residual_quantize_mxfp8 - RFQ with an MXFP8 second path: Q(X) in
+ *   MXFP4, R = X - deq(Q(X)) exactly in fp32, Q(R) in MXFP8.
+ *   qx_codes [M, K/2], qx_scales [M, K/32]: Q(X), MXFP4.  (out, device)
+ *   qr_codes [M, K],   qr_scales [M, K/32]: Q(R), MXFP8.  (out, device)
+ *   Other arguments as rfq_residual_quantize.
+ *
+ * rfq_gemm_w4a8 - Y = deq(QX8) deq(W)^T for MXFP8 activation codes
+ *   qx_codes [M, K] / qx_scales [M, K/32] and the MXFP4 weight; fp32
+ *   accumulation. Other arguments and errors as rfq_gemm_w4a4.
+ *
+ * rfq_gemm_w4a4_mxfp8_residual - the RFQ GEMM with an MXFP8 residual term:
+ *   Y = deq(QX) deq(W)^T + deq(QR8) deq(W)^T in one fp32 accumulator, for
+ *   QX MXFP4 ([M, K/2] codes) and QR8 MXFP8 ([M, K] codes) as written by
+ *   rfq_residual_quantize_mxfp8. Other arguments and errors as rfq_gemm_w4a4
+ *   (qr_codes/qr_scales must not be NULL).
+ */
+rfq_status_t rfq_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
+                                uint8_t* codes, uint8_t* scales, rfq_stream_t stream);
+rfq_status_t rfq_residual_quantize_mxfp8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                         uint8_t* qx_codes, uint8_t* qx_scales,
+                                         uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream);
+rfq_status_t rfq_gemm_w4a8(const uint8_t* qx_codes, const uint8_t* qx_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales,
+                           int64_t M, int64_t N, int64_t K,
+                           void* y, int y_dtype, int64_t ldy, rfq_stream_t stream);
+rfq_status_t rfq_gemm_w4a4_mxfp8_residual(const uint8_t* qx_codes, const uint8_t* qx_scales,
+                                          const uint8_t* qr_codes, const uint8_t* qr_scales,
+                                          const uint8_t* w_codes, const uint8_t* w_scales,
+                                          int64_t M, int64_t N, int64_t K,
+                                          void* y, int y_dtype, int64_t ldy, rfq_stream_t stream);
 
 /* Bytes of workspace rfq_linear needs for an [M, K] activation: Q(X) and
  * Q(R) codes and scales, each region rounded up to 256 bytes. Host only;

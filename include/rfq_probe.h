@@ -42,6 +42,17 @@ extern "C" {
 rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
                                     int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream);
 
+/*
+ * rfq_probe_mfma_ceiling_e4m3 - the same loop with the second operand in
+ * E4M3 (the instruction of the MXFP8 activation variants: MXFP4 weight first,
+ * MXFP8 activation second). Each lane loads eight 16-byte pieces of b_codes
+ * (two per operand, 32 bytes) at consecutive positions modulo its size; all
+ * else as rfq_probe_mfma_ceiling, including the flop count per call.
+ */
+rfq_status_t rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes,
+                                         size_t b_bytes, int workgroups, int iters, uint64_t* stamps, float* sink,
+                                         rfq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

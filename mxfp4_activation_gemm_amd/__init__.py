@@ -5,6 +5,9 @@ Recovery for Quantized Multimodal LLMs", §1): X is quantized to MXFP4, the
 full error R = X - deq(Q(X)) is quantized to MXFP4 again, and
 Y = Q(X) Wq^T + Q(R) Wq^T is one K-doubled block-scaled FP4 GEMM.
 
+MXFP8 variants (E4M3 elements): W4A8 (activation in MXFP8, no residual) and
+RFQ whose second path quantizes R to MXFP8; the weight stays MXFP4.
+
 This module only marshals torch tensors (device memory and the current HIP
 stream) into the C ABI of include/rfq.h; every step runs in the HIP kernels of
 librfq.so. Nothing falls back to CPU or PyTorch compute: if the library is
@@ -21,6 +24,12 @@ __all__ = [
     "quantize_mxfp4",
     "residual_quantize",
     "gemm_w4a4",
+    "rotate_residual_quantize",
+    "rotate_quantize_weight",
+    "quantize_mxfp8",
+    "residual_quantize_mxfp8",
+    "gemm_w4a8",
+    "gemm_w4a4_mxfp8_residual",
     "linear",
     "linear_workspace_size",
     "library",
@@ -57,18 +66,18 @@ def _y_dtype(out_dtype):
     raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
 
 
-def _quantize(fn, x):
+def _quantize(fn, x, bytes_per_element=0.5):
     rows, K, ldx, dt = _x_args(x)
-    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    codes = torch.empty((rows, int(K * bytes_per_element)), dtype=torch.uint8, device=x.device)
     scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
     check(fn(_ptr(x), dt, rows, K, ldx, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
 
 
-def _residual(fn, x):
+def _residual(fn, x, r_bytes_per_element=0.5):
     M, K, ldx, dt = _x_args(x)
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-    qr = torch.empty_like(qx)
+    qr = torch.empty((M, int(K * r_bytes_per_element)), dtype=torch.uint8, device=x.device)
     sx = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     sr = torch.empty_like(sx)
     check(fn(_ptr(x), dt, M, K, ldx, _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), _stream()))
@@ -95,19 +104,62 @@ def rotate_quantize_weight(w):
     return _quantize(load().rfq_rotate_quantize_weight, w)
 
 
+def _codes_ok(*ts):
+    for t in ts:
+        if t is not None and (t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
+
+
+def _out(y, M, N, out_dtype, device):
+    y = y if y is not None else torch.empty((M, N), dtype=out_dtype, device=device)
+    if y.stride(1) != 1:
+        raise ValueError("out must have unit stride along N")
+    return y
+
+
 def gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.bfloat16, out=None):
     """Y = deq(QX) deq(W)^T + deq(QR) deq(W)^T (qr = sr = None: plain W4A4)."""
     M, N, K = qx.shape[0], wq.shape[0], qx.shape[1] * 2
-    for t in (qx, sx, qr, sr, wq, sw):
-        if t is not None and (t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda):
-            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
+    _codes_ok(qx, sx, qr, sr, wq, sw)
     if wq.shape[1] * 2 != K:
         raise ValueError("QX and W disagree on K")
-    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=qx.device)
-    if y.stride(1) != 1:
-        raise ValueError("out must have unit stride along N")
+    y = _out(out, M, N, out_dtype, qx.device)
     check(load().rfq_gemm_w4a4(_ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), _ptr(wq), _ptr(sw), M, N, K, _ptr(y),
                                _y_dtype(y.dtype), y.stride(0), _stream()))
+    return y
+
+
+def quantize_mxfp8(x):
+    """MXFP8 (E4M3) along K of bf16 or fp32 X: (codes uint8 [rows, K], scales uint8 [rows, K/32])."""
+    return _quantize(load().rfq_quantize_mxfp8, x, bytes_per_element=1)
+
+
+def residual_quantize_mxfp8(x):
+    """RFQ encoding with an MXFP8 second path: (qx [M, K/2], sx, qr8 [M, K], sr)."""
+    return _residual(load().rfq_residual_quantize_mxfp8, x, r_bytes_per_element=1)
+
+
+def gemm_w4a8(qx8, sx, wq, sw, out_dtype=torch.bfloat16, out=None):
+    """Y = deq(QX8) deq(W)^T for MXFP8 activation codes and the MXFP4 weight."""
+    M, N, K = qx8.shape[0], wq.shape[0], qx8.shape[1]
+    _codes_ok(qx8, sx, wq, sw)
+    if wq.shape[1] * 2 != K:
+        raise ValueError("QX and W disagree on K")
+    y = _out(out, M, N, out_dtype, qx8.device)
+    check(load().rfq_gemm_w4a8(_ptr(qx8), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _y_dtype(y.dtype),
+                               y.stride(0), _stream()))
+    return y
+
+
+def gemm_w4a4_mxfp8_residual(qx, sx, qr8, sr, wq, sw, out_dtype=torch.bfloat16, out=None):
+    """Y = deq(QX) deq(W)^T + deq(QR8) deq(W)^T, QX MXFP4 and QR8 MXFP8."""
+    M, N, K = qx.shape[0], wq.shape[0], qx.shape[1] * 2
+    _codes_ok(qx, sx, qr8, sr, wq, sw)
+    if wq.shape[1] * 2 != K or qr8.shape[1] != K:
+        raise ValueError("operands disagree on K")
+    y = _out(out, M, N, out_dtype, qx.device)
+    check(load().rfq_gemm_w4a4_mxfp8_residual(_ptr(qx), _ptr(sx), _ptr(qr8), _ptr(sr), _ptr(wq), _ptr(sw), M, N, K,
+                                              _ptr(y), _y_dtype(y.dtype), y.stride(0), _stream()))
     return y
 
 

@@ -97,18 +97,18 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 namespace {
 
 rfq_status_t quantize_common(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
-                             uint8_t* scales, int rotate, rfq_stream_t stream) {
+                             uint8_t* scales, int rotate, int fmt, rfq_stream_t stream) {
   RFQ_TRY(check_rows_k(rows, K, "rows"));
   RFQ_TRY(check_dtype(x_dtype));
   if (rows == 0) return ok();
   RFQ_TRY(check_x(x, x_dtype, K, ldx));
   RFQ_TRY(check_codes(codes, scales, "output"));
-  return launched(rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, rotate, rows, K, ldx, codes, scales, nullptr,
-                                       nullptr, static_cast<hipStream_t>(stream)));
+  return launched(rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, rotate, fmt, 0, rows, K, ldx, codes, scales,
+                                       nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 rfq_status_t residual_common(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* qx_codes,
-                             uint8_t* qx_scales, uint8_t* qr_codes, uint8_t* qr_scales, int rotate,
+                             uint8_t* qx_scales, uint8_t* qr_codes, uint8_t* qr_scales, int rotate, int r_fmt,
                              rfq_stream_t stream) {
   RFQ_TRY(check_rows_k(M, K, "M"));
   RFQ_TRY(check_dtype(x_dtype));
@@ -116,8 +116,28 @@ rfq_status_t residual_common(const void* x, int x_dtype, int64_t M, int64_t K, i
   RFQ_TRY(check_x(x, x_dtype, K, ldx));
   RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
   RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
-  return launched(rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, rotate, M, K, ldx, qx_codes, qx_scales, qr_codes,
-                                       qr_scales, static_cast<hipStream_t>(stream)));
+  return launched(rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, rotate, 4, r_fmt, M, K, ldx, qx_codes, qx_scales,
+                                       qr_codes, qr_scales, static_cast<hipStream_t>(stream)));
+}
+
+// Shared checks and launch of the GEMM entry points: activation formats
+// x_fmt / r_fmt (4: MXFP4, 8: MXFP8; r_fmt 0 without a residual term).
+rfq_status_t gemm_common(int x_fmt, int r_fmt, const uint8_t* qx_codes, const uint8_t* qx_scales,
+                         const uint8_t* qr_codes, const uint8_t* qr_scales, const uint8_t* w_codes,
+                         const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int64_t ldy,
+                         rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_rows_k(N, K, "N"));
+  if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
+  if (M == 0 || N == 0) return ok();
+  RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
+  if (r_fmt != 0) RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
+  RFQ_TRY(check_codes(w_codes, w_scales, "W"));
+  RFQ_TRY(check_y(y, y_dtype, N, ldy));
+  return launched(rfq::launch_gemm(x_fmt, r_fmt, qx_codes, qx_scales, r_fmt ? qr_codes : nullptr,
+                                   r_fmt ? qr_scales : nullptr, w_codes, w_scales, M, N, K, y,
+                                   y_dtype == RFQ_DTYPE_BF16, ldy, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -126,24 +146,35 @@ extern "C" {
 
 rfq_status_t rfq_quantize_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
                                 uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
-  return quantize_common(x, x_dtype, rows, K, ldx, codes, scales, 0, stream);
+  return quantize_common(x, x_dtype, rows, K, ldx, codes, scales, 0, 4, stream);
+}
+
+rfq_status_t rfq_quantize_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t ldx,
+                                uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
+  return quantize_common(x, x_dtype, rows, K, ldx, codes, scales, 0, 8, stream);
 }
 
 rfq_status_t rfq_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                    uint8_t* qx_codes, uint8_t* qx_scales,
                                    uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream) {
-  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 0, stream);
+  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 0, 4, stream);
+}
+
+rfq_status_t rfq_residual_quantize_mxfp8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                         uint8_t* qx_codes, uint8_t* qx_scales,
+                                         uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream) {
+  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 0, 8, stream);
 }
 
 rfq_status_t rfq_rotate_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                           uint8_t* qx_codes, uint8_t* qx_scales,
                                           uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream) {
-  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 1, stream);
+  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 1, 4, stream);
 }
 
 rfq_status_t rfq_rotate_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
                                         uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
-  return quantize_common(w, w_dtype, N, K, ldw, codes, scales, 2, stream);
+  return quantize_common(w, w_dtype, N, K, ldw, codes, scales, 2, 4, stream);
 }
 
 rfq_status_t rfq_gemm_w4a4(const uint8_t* qx_codes, const uint8_t* qx_scales,
@@ -151,19 +182,26 @@ rfq_status_t rfq_gemm_w4a4(const uint8_t* qx_codes, const uint8_t* qx_scales,
                            const uint8_t* w_codes, const uint8_t* w_scales,
                            int64_t M, int64_t N, int64_t K,
                            void* y, int y_dtype, int64_t ldy, rfq_stream_t stream) {
-  RFQ_TRY(check_rows_k(M, K, "M"));
-  RFQ_TRY(check_rows_k(N, K, "N"));
-  if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
-    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
-  if (M == 0 || N == 0) return ok();
-  RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
   if ((qr_codes == nullptr) != (qr_scales == nullptr))
     return fail(RFQ_ERR_NULL_POINTER, "Q(R) codes and scales must be both NULL (plain W4A4) or both set");
-  if (qr_codes != nullptr) RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
-  RFQ_TRY(check_codes(w_codes, w_scales, "W"));
-  RFQ_TRY(check_y(y, y_dtype, N, ldy));
-  return launched(rfq::launch_gemm(qx_codes, qx_scales, qr_codes, qr_scales, w_codes, w_scales, M, N, K, y,
-                                   y_dtype == RFQ_DTYPE_BF16, ldy, static_cast<hipStream_t>(stream)));
+  return gemm_common(4, qr_codes != nullptr ? 4 : 0, qx_codes, qx_scales, qr_codes, qr_scales, w_codes, w_scales, M,
+                     N, K, y, y_dtype, ldy, stream);
+}
+
+rfq_status_t rfq_gemm_w4a8(const uint8_t* qx_codes, const uint8_t* qx_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales,
+                           int64_t M, int64_t N, int64_t K,
+                           void* y, int y_dtype, int64_t ldy, rfq_stream_t stream) {
+  return gemm_common(8, 0, qx_codes, qx_scales, nullptr, nullptr, w_codes, w_scales, M, N, K, y, y_dtype, ldy, stream);
+}
+
+rfq_status_t rfq_gemm_w4a4_mxfp8_residual(const uint8_t* qx_codes, const uint8_t* qx_scales,
+                                          const uint8_t* qr_codes, const uint8_t* qr_scales,
+                                          const uint8_t* w_codes, const uint8_t* w_scales,
+                                          int64_t M, int64_t N, int64_t K,
+                                          void* y, int y_dtype, int64_t ldy, rfq_stream_t stream) {
+  return gemm_common(4, 8, qx_codes, qx_scales, qr_codes, qr_scales, w_codes, w_scales, M, N, K, y, y_dtype, ldy,
+                     stream);
 }
 
 size_t rfq_linear_workspace_size(int64_t M, int64_t K) {
@@ -198,9 +236,10 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
   uint8_t* qr = sx + scales;
   uint8_t* sr = qr + codes;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, 0, M, K, ldx, qx, sx, qr, sr, s);
+  hipError_t e = rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, 0, 4, 4, M, K, ldx, qx, sx, qr, sr, s);
   if (e != hipSuccess) return launched(e);
-  return launched(rfq::launch_gemm(qx, sx, qr, sr, w_codes, w_scales, M, N, K, y, y_dtype == RFQ_DTYPE_BF16, ldy, s));
+  return launched(rfq::launch_gemm(4, 4, qx, sx, qr, sr, w_codes, w_scales, M, N, K, y, y_dtype == RFQ_DTYPE_BF16, ldy,
+                                   s));
 }
 
 const char* rfq_status_string(rfq_status_t status) {
@@ -221,8 +260,12 @@ const char* rfq_last_error_detail(void) { return g_detail.c_str(); }
 
 int rfq_abi_version(void) { return RFQ_ABI_VERSION; }
 
-rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
-                                    int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+rfq_status_t probe_common(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes, int b_fmt,
+                          int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream) {
   if (a_codes == nullptr || b_codes == nullptr || stamps == nullptr || sink == nullptr)
     return fail(RFQ_ERR_NULL_POINTER, "probe buffers must not be NULL");
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return fail(RFQ_ERR_MISALIGNED, "operands must be 16-byte aligned");
@@ -231,8 +274,23 @@ rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, cons
     return fail(RFQ_ERR_INVALID_SHAPE, "operand sizes must be multiples of 16 in [16, 2^36)");
   if (workgroups <= 0 || workgroups > 65536 || iters <= 0)
     return fail(RFQ_ERR_INVALID_SHAPE, "workgroups must be in [1, 65536] and iters positive");
-  return launched(rfq::launch_mfma_ceiling(a_codes, a_bytes, b_codes, b_bytes, workgroups, iters, stamps, sink,
+  return launched(rfq::launch_mfma_ceiling(a_codes, a_bytes, b_codes, b_bytes, b_fmt, workgroups, iters, stamps, sink,
                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
+                                    int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream) {
+  return probe_common(a_codes, a_bytes, b_codes, b_bytes, 4, workgroups, iters, stamps, sink, stream);
+}
+
+rfq_status_t rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes,
+                                         size_t b_bytes, int workgroups, int iters, uint64_t* stamps, float* sink,
+                                         rfq_stream_t stream) {
+  return probe_common(a_codes, a_bytes, b_codes, b_bytes, 8, workgroups, iters, stamps, sink, stream);
 }
 
 }  // extern "C"

@@ -73,35 +73,80 @@ constexpr int kScaleRowBytes = 16;
 constexpr uint32_t kOOB = 0x80000000u;              // voffset that is always out of range
 constexpr int kGroupM = 4;                          // tile rows swept together (L2 reuse)
 
-// An output tile of BM x BN on `Waves` waves (grid Waves/2 x 2); Occ
-// workgroups are meant to share a CU, and LDS and registers are sized so.
-template <int BM_, int BN_, int Waves_, int Occ_>
+// Operand formats of one GEMM variant. The activation side has one or two
+// terms, X and (for RFQ) the residual R, each E2M1 (4) or E4M3 (8); the
+// weight is E2M1. In LDS a stage row of an E2M1 term is one 64-byte sub-tile
+// (128 elements); an E4M3 term's 128 bytes are two sub-tiles.
+//
+// E4M3 operand layout of the instruction (checked on hardware with one-hot
+// operands and distinct per-lane scales): per row and 64-wide K step, lane
+// half h holds elements 16 h .. 16 h + 15 of K-block 0 in its bytes 0..15 and
+// the same elements of K-block 1 in bytes 16..31; the scale of K-block b is
+// the one supplied by lane half b. (E2M1 operands hold K-block h whole in
+// lane half h.) So the two sub-tiles of an E4M3 term hold, at LDS chunk c =
+// 2 s + lhalf (the chunk an MFMA lane reads in step s), the 16-byte row
+// chunks 4 s + lhalf (first sub-tile) and 4 s + 2 + lhalf (second): row chunk
+// 4 (c / 2) + (c % 2), plus 2 for the second sub-tile.
+template <int kX, int kR>
+struct Fmts {
+  static constexpr int kXFmt = kX, kRFmt = kR;
+  static constexpr bool kResid = kR != 0;
+  static constexpr int kXSub = kX == 8 ? 2 : 1;
+  static constexpr int kRSub = kR == 8 ? 2 : (kR == 4 ? 1 : 0);
+  static constexpr int kSubA = kXSub + kRSub;          // activation sub-tiles per stage
+  static constexpr int kScalesA = kResid ? 2 : 1;      // activation scale streams
+  static constexpr int kTerms = kResid ? 2 : 1;        // MFMAs per output tile per step
+  static_assert((kX == 4 || kX == 8) && (kR == 0 || kR == 4 || kR == 8) && !(kX == 8 && kR != 0), "formats");
+};
+using FmtW4A4 = Fmts<4, 0>;
+using FmtRfq = Fmts<4, 4>;
+using FmtW4A8 = Fmts<8, 0>;
+using FmtRfq8 = Fmts<4, 8>;
+
+// MFMA format code of an element format: E4M3 is 0, E2M1 is 4.
+template <int kFmt>
+constexpr int kMfmaFmt = kFmt == 8 ? 0 : 4;
+
+// An output tile of BM x BN on `Waves` waves (grid Waves/2 x 2) for the
+// operand formats F; Occ workgroups are meant to share a CU, and LDS and
+// registers are sized so.
+template <int BM_, int BN_, int Waves_, int Occ_, class F>
 struct TileCfg {
   static constexpr int kBM = BM_, kBN = BN_, kWaves = Waves_, kOcc = Occ_;
   static constexpr int kWavesM = kWaves / kWavesN;
   static constexpr int kWaveM = kBM / kWavesM, kWaveN = kBN / kWavesN;
   static constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;           // MFMA tiles per wave
-  static constexpr int kTileBytesA = kBM * kRowBytes, kTileBytesB = kBN * kRowBytes;
-  static constexpr int kStageBytes = 2 * kTileBytesA + kTileBytesB;    // X, R, W
+  static constexpr int kTileBytesA = kBM * kRowBytes, kTileBytesB = kBN * kRowBytes;   // one sub-tile
+  static constexpr int kStageBytes = F::kSubA * kTileBytesA + kTileBytesB;
   static constexpr int kScaleBytesA = kBM * kScaleRowBytes;
-  static constexpr int kScaleBytes = 2 * kScaleBytesA + kBN * kScaleRowBytes;
+  static constexpr int kScaleBytes = F::kScalesA * kScaleBytesA + kBN * kScaleRowBytes;
   static constexpr int kLdsBytes = kRing * kStageBytes + kScaleBytes;
-  static constexpr int kLoadsA = kBM / 16 / kWaves;    // 16-row DMA instructions per wave for X (and R)
+  static constexpr int kLoadsA = kBM / 16 / kWaves;    // 16-row DMA instructions per wave per sub-tile of X / R
   static constexpr int kLoadsB = kBN / 16 / kWaves;    // for W
   static_assert(kTM >= 1 && kTN >= 1 && kLoadsA >= 1 && kLoadsB >= 1, "tile shape");
   static_assert(kLdsBytes * kOcc <= 160 * 1024, "LDS budget per CU");
 };
-// 256 x 256 outputs, 8 waves of 64 x 128 (128 accumulators each), one
-// workgroup per CU, 156 KB of LDS: the main tile.
-using BigTile = TileCfg<256, 256, 8, 1>;
-// 128 x 128 outputs, 4 waves of 64 x 64, two workgroups per CU (78 KB of LDS
-// each): quadrants of big tiles, for the last partial round of a launch.
-using QuadTile = TileCfg<128, 128, 4, 2>;
+// Main tiles: 256 x 256 outputs, 8 waves of 64 x 128 (128 accumulators
+// each), one workgroup per CU (up to 156 KB of LDS); for the last partial
+// round of a launch, quadrants of 128 x 128 on 4 waves, two per CU. With an
+// E4M3 residual (three activation sub-tiles) the stage would not fit three
+// deep, so that variant uses 128 x 256 tiles (8 waves of 32 x 128) and
+// 64 x 128 quadrants.
+template <class F, bool kNarrow = (F::kSubA > 2)>
+struct Tiles {
+  using Big = TileCfg<256, 256, 8, 1, F>;
+  using Quad = TileCfg<128, 128, 4, 2, F>;
+};
+template <class F>
+struct Tiles<F, true> {
+  using Big = TileCfg<128, 256, 8, 1, F>;
+  using Quad = TileCfg<64, 128, 4, 2, F>;
+};
 
 struct GemmParams {
-  const uint8_t* qx;
+  const uint8_t* qx;      // X codes: K/2 bytes per row (E2M1) or K (E4M3)
   const uint8_t* sx;
-  const uint8_t* qr;
+  const uint8_t* qr;      // R codes, likewise by format (RFQ variants)
   const uint8_t* sr;
   const uint8_t* w;
   const uint8_t* sw;
@@ -187,24 +232,39 @@ __device__ __forceinline__ void tile_origin(const GemmParams& p, int bid, int& m
   n0 = tn * p.gn + (q % 2) * (p.gn / 2);
 }
 
-template <int S, bool kResid, int kTM, int kTN>
-__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x4_t (&ax)[kTM],
-                                          const i32x4_t (&ar)[kTM], const i32x4_t (&b)[kTN],
-                                          const uint32_t (&scx)[kTM], const uint32_t (&scr)[kTM],
-                                          const uint32_t (&scw)[kTN]) {
+// The MFMA operand of one activation term for fragment row group i: an E2M1
+// term is one 16-byte fragment (the low half of the operand registers), an
+// E4M3 term the fragments of its first and second sub-tiles, in that order.
+template <int kFmt, int kSub, int kSubA, int kTM>
+__device__ __forceinline__ i32x8_t term_operand(const i32x4_t (&a)[kSubA][kTM], int i) {
+  if constexpr (kFmt == 8)
+    return i32x8_t{a[kSub][i].x, a[kSub][i].y, a[kSub][i].z, a[kSub][i].w,
+                   a[kSub + 1][i].x, a[kSub + 1][i].y, a[kSub + 1][i].z, a[kSub + 1][i].w};
+  else
+    return widen(a[kSub][i]);
+}
+
+template <int S, class F, int kTM, int kTN>
+__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x4_t (&a)[F::kSubA][kTM],
+                                          const i32x4_t (&b)[kTN], const uint32_t (&scx)[kTM],
+                                          const uint32_t (&scr)[kTM], const uint32_t (&scw)[kTN]) {
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+  for (int i = 0; i < kTM; ++i) {
+    const i32x8_t ax = term_operand<F::kXFmt, 0, F::kSubA, kTM>(a, i);
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(b[j]), widen(ax[i]), acc[i][j], 4, 4, 2 * S,
-                                                                  (int)scw[j], 2 * S, (int)scx[i]);
-  if (kResid) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(b[j]), ax, acc[i][j], 4, kMfmaFmt<F::kXFmt>,
+                                                                  2 * S, (int)scw[j], 2 * S, (int)scx[i]);
+  }
+  if constexpr (F::kResid) {
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
+    for (int i = 0; i < kTM; ++i) {
+      const i32x8_t ar = term_operand<F::kRFmt, F::kXSub, F::kSubA, kTM>(a, i);
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(b[j]), widen(ar[i]), acc[i][j], 4, 4, 2 * S,
-                                                                    (int)scw[j], 2 * S, (int)scr[i]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(b[j]), ar, acc[i][j], 4, kMfmaFmt<F::kRFmt>,
+                                                                    2 * S, (int)scw[j], 2 * S, (int)scr[i]);
+    }
   }
 }
 
@@ -232,9 +292,11 @@ __device__ __forceinline__ void interleave_hint() {
 // kStream (needs kFast): every tile of the launch lies inside Y and Y takes
 // vector stores, and each workgroup streams several tiles; otherwise each
 // workgroup computes one tile and stores it with per-element bounds checks.
-template <class C, bool kResid, bool kOutBf16, bool kFast, bool kStream>
+template <class C, class F, bool kOutBf16, bool kFast, bool kStream>
 __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParams p) {
   static_assert(kFast || !kStream, "streaming needs whole scale groups");
+  constexpr bool kResid = F::kResid;
+  constexpr int kSubA = F::kSubA;
   constexpr int kBM = C::kBM, kBN = C::kBN, kWaves = C::kWaves;
   constexpr int kWaveM = C::kWaveM, kWaveN = C::kWaveN, kTM = C::kTM, kTN = C::kTN;
   constexpr int kTileBytesA = C::kTileBytesA, kStageBytes = C::kStageBytes;
@@ -258,17 +320,24 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   int cm0, cn0;                                  // origin of the tile being computed
   tile_origin(p, blockIdx.x, cm0, cn0);
   if (cm0 >= p.M || cn0 >= p.N) return;          // a quadrant past the edge (whole workgroup)
-  const uint32_t kbytes = (uint32_t)p.K / 2, kblocks = (uint32_t)p.K / 32;
   const int nstages = (p.K + kBK - 1) / kBK;
   const int ngroups = (nstages + kScaleGroup - 1) / kScaleGroup;
   const int total_stages = ntiles * nstages;
 
-  // Buffer descriptors of the tile being fetched (rows past the tensor read as zero).
-  __amdgpu_buffer_rsrc_t rx, rr, rw, rsx, rsr, rsw;
+  // Buffer descriptors of the tile being fetched (rows past the tensor read
+  // as zero), one per activation sub-tile: an E4M3 term's second sub-tile
+  // starts 32 bytes (two chunks) into the row, so the same offsets fetch it.
+  const uint32_t kbytes = (uint32_t)p.K / 2, kblocks = (uint32_t)p.K / 32;
+  __amdgpu_buffer_rsrc_t ra[kSubA], rw, rsx, rsr, rsw;
   auto set_load_tile = [&](const GemmParams& q, int m0, int n0) {
     const uint32_t rows_a = (uint32_t)min(kBM, q.M - m0), rows_b = (uint32_t)min(kBN, q.N - n0);
-    rx = make_rsrc(q.qx + (int64_t)m0 * kbytes, rows_a * kbytes);
-    rr = make_rsrc(kResid ? q.qr + (int64_t)m0 * kbytes : q.qx, rows_a * kbytes);
+    const uint32_t xrow = F::kXFmt == 8 ? 2 * kbytes : kbytes, rrow = F::kRFmt == 8 ? 2 * kbytes : kbytes;
+    ra[0] = make_rsrc(q.qx + (int64_t)m0 * xrow, rows_a * xrow);
+    if constexpr (F::kXFmt == 8) ra[1] = make_rsrc(q.qx + (int64_t)m0 * xrow + 32, rows_a * xrow - 32);
+    if constexpr (F::kResid) {
+      ra[F::kXSub] = make_rsrc(q.qr + (int64_t)m0 * rrow, rows_a * rrow);
+      if constexpr (F::kRFmt == 8) ra[F::kXSub + 1] = make_rsrc(q.qr + (int64_t)m0 * rrow + 32, rows_a * rrow - 32);
+    }
     rw = make_rsrc(q.w + (int64_t)n0 * kbytes, rows_b * kbytes);
     rsx = make_rsrc(q.sx + (int64_t)m0 * kblocks, rows_a * kblocks);
     rsr = make_rsrc(kResid ? q.sr + (int64_t)m0 * kblocks : q.sx, rows_a * kblocks);
@@ -277,15 +346,16 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   set_load_tile(p, cm0, cn0);
   int load_tile = 0, load_base = 0;              // tile being fetched and its first stream stage
 
-  // Code-tile loads: wave w fetches rows [BM/waves w, BM/waves (w + 1)) of X
-  // and R and the matching range of W's BN rows, 16 rows per instruction;
-  // lane l takes row 16 n + l / 4 of them and chunk (l % 4) ^ f(row).
-  uint32_t lda_voff[C::kLoadsA], lda_chunk[C::kLoadsA], ldb_voff[C::kLoadsB], ldb_chunk[C::kLoadsB];
+  // Code-tile loads: wave w fetches rows [BM/waves w, BM/waves (w + 1)) of
+  // each activation sub-tile and the matching range of W's BN rows, 16 rows
+  // per instruction; lane l takes row 16 n + l / 4 of them and LDS chunk
+  // c = (l % 4) ^ f(row), which is row chunk c of an E2M1 sub-tile and row
+  // chunk 4 (c / 2) + c % 2 (+ 2 in the second sub-tile) of an E4M3 term.
+  uint32_t lda_chunk[C::kLoadsA], lda_row[C::kLoadsA], ldb_voff[C::kLoadsB], ldb_chunk[C::kLoadsB];
 #pragma unroll
   for (int n = 0; n < C::kLoadsA; ++n) {
-    const uint32_t row = kBM / kWaves * wave + 16 * n + (lane >> 2);
-    lda_chunk[n] = (lane & 3) ^ swz(row);
-    lda_voff[n] = row * kbytes + 16 * lda_chunk[n];
+    lda_row[n] = kBM / kWaves * wave + 16 * n + (lane >> 2);
+    lda_chunk[n] = (lane & 3) ^ swz(lda_row[n]);
   }
 #pragma unroll
   for (int n = 0; n < C::kLoadsB; ++n) {
@@ -293,16 +363,22 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     ldb_chunk[n] = (lane & 3) ^ swz(row);
     ldb_voff[n] = row * kbytes + 16 * ldb_chunk[n];
   }
-  constexpr int kDmaPerStage = (kResid ? 2 : 1) * C::kLoadsA + C::kLoadsB;
-  constexpr int kMfmaPerStep = kTM * kTN * (kResid ? 2 : 1);
-  constexpr int kReadsPerStep = kTM * (kResid ? 2 : 1) + kTN;
-  constexpr int kScaleRowReads = kTM * (kResid ? 2 : 1) + kTN;
+  // byte offset of a lane's chunk in stage 0 of an activation term of format kFmt
+  auto lda_voff = [&](auto fmt_c, int n) -> uint32_t {
+    constexpr int fmt = decltype(fmt_c)::value;
+    return fmt == 8 ? lda_row[n] * (2 * kbytes) + 64 * (lda_chunk[n] >> 1) + 16 * (lda_chunk[n] & 1)
+                    : lda_row[n] * kbytes + 16 * lda_chunk[n];
+  };
+  constexpr int kDmaPerStage = kSubA * C::kLoadsA + C::kLoadsB;
+  constexpr int kMfmaPerStep = kTM * kTN * F::kTerms;
+  constexpr int kReadsPerStep = kTM * kSubA + kTN;
+  constexpr int kScaleRowReads = kTM * F::kScalesA + kTN;
   // scale pieces (64 rows x 16 B) per group: BM/64 for X and for R, BN/64
   // for W, dealt round the waves; when they do not divide evenly the spare
   // slots repeat pieces (identical bytes to the same place), so every wave
   // issues as many loads
   constexpr int kPiecesA = kBM / 64, kPiecesB = kBN / 64;
-  constexpr int kPieces = (kResid ? 2 : 1) * kPiecesA + kPiecesB;
+  constexpr int kPieces = F::kScalesA * kPiecesA + kPiecesB;
   constexpr int kScaleLoadsPerWave = (kPieces + kWaves - 1) / kWaves;
 
   // Stream stage st (stage st - load_base of the tile being fetched). A
@@ -314,24 +390,32 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     constexpr int part = decltype(part_c)::value;   // 0: first kPart0 loads, 1: the rest, 2: all
     uint8_t* buf = ring + (st % kRing) * kStageBytes;
     const int kst = st - load_base;
-    const uint32_t kb = (uint32_t)kst * kRowBytes;
     const bool past_end = st >= total_stages;
 #pragma unroll
     for (int n = 0; n < C::kLoadsA; ++n) {
-      uint32_t vo = lda_voff[n] + kb;
-      if ((!kFast && (uint32_t)kst * (kBK / 32) + lda_chunk[n] >= kblocks) || past_end) vo = kOOB;
       uint8_t* dst = buf + (kBM / kWaves * wave + 16 * n) * kRowBytes;
-      const int ix = (kResid ? 2 : 1) * n;
-      if (part == 2 || (ix < kPart0) == (part == 0)) load16_to_lds(rx, dst, vo);
-      if (kResid && (part == 2 || (ix + 1 < kPart0) == (part == 0))) load16_to_lds(rr, dst + kTileBytesA, vo);
+#pragma unroll
+      for (int t = 0; t < kSubA; ++t) {
+        const bool is_x = t < F::kXSub;
+        const bool fp8 = is_x ? F::kXFmt == 8 : F::kRFmt == 8;
+        const bool second = fp8 && t == (is_x ? 1 : F::kXSub + 1);
+        // K-block (within the stage) of this lane's chunk: c for E2M1; for
+        // E4M3 2 (c / 2), + 1 in the second sub-tile
+        const uint32_t blk = fp8 ? 2 * (lda_chunk[n] >> 1) + (second ? 1 : 0) : lda_chunk[n];
+        uint32_t vo = fp8 ? lda_voff(std::integral_constant<int, 8>{}, n) + (uint32_t)kst * (2 * kRowBytes)
+                          : lda_voff(std::integral_constant<int, 4>{}, n) + (uint32_t)kst * kRowBytes;
+        if ((!kFast && (uint32_t)kst * (kBK / 32) + blk >= kblocks) || past_end) vo = kOOB;
+        const int ix = kSubA * n + t;
+        if (part == 2 || (ix < kPart0) == (part == 0)) load16_to_lds(ra[t], dst + t * kTileBytesA, vo);
+      }
     }
 #pragma unroll
     for (int n = 0; n < C::kLoadsB; ++n) {
-      uint32_t vo = ldb_voff[n] + kb;
+      uint32_t vo = ldb_voff[n] + (uint32_t)kst * kRowBytes;
       if ((!kFast && (uint32_t)kst * (kBK / 32) + ldb_chunk[n] >= kblocks) || past_end) vo = kOOB;
-      const int ix = (kResid ? 2 : 1) * C::kLoadsA + n;
+      const int ix = kSubA * C::kLoadsA + n;
       if (part == 2 || (ix < kPart0) == (part == 0))
-        load16_to_lds(rw, buf + 2 * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo);
+        load16_to_lds(rw, buf + kSubA * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo);
     }
   };
 
@@ -374,7 +458,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       else if (kResid && j < 2 * kPiecesA)
         issue_scale_piece(rsr, g, 1, j - kPiecesA);
       else
-        issue_scale_piece(rsw, g, 2, j - (kResid ? 2 : 1) * kPiecesA);
+        issue_scale_piece(rsw, g, F::kScalesA, j - F::kScalesA * kPiecesA);
     }
   };
 
@@ -385,7 +469,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   for (int s = 0; s < 2; ++s) rd_off[s] = lrow * kRowBytes + 16 * ((2 * s + lhalf) ^ swz(lrow));
   const uint32_t a_row0 = kWaveM * wm, b_row0 = kWaveN * wn;
 
-  auto read_step = [&](int st, int s, i32x4_t (&ax)[kTM], i32x4_t (&ar)[kTM], i32x4_t (&bw)[kTN]) {
+  auto read_step = [&](int st, int s, i32x4_t (&a)[kSubA][kTM], i32x4_t (&bw)[kTN]) {
     // one lane offset per step plus a scalar slot base; every fragment then
     // sits at a constant distance from it (an instruction offset). (The lane
     // offset is re-read here so that the compiler does not keep a separate
@@ -396,11 +480,11 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const uint8_t* src = buf + (a_row0 + 32 * i) * kRowBytes;
-      ax[i] = read_frag(src);
-      if (kResid) ar[i] = read_frag(src + kTileBytesA);
+#pragma unroll
+      for (int t = 0; t < kSubA; ++t) a[t][i] = read_frag(src + t * kTileBytesA);
     }
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) bw[j] = read_frag(buf + 2 * kTileBytesA + (b_row0 + 32 * j) * kRowBytes);
+    for (int j = 0; j < kTN; ++j) bw[j] = read_frag(buf + kSubA * kTileBytesA + (b_row0 + 32 * j) * kRowBytes);
   };
   // this lane's scale words for two stages (a pair of the group's four)
   i32x2_t gx[kTM], gr[kTM], gw[kTN];
@@ -413,7 +497,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     }
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
-      gw[j] = *reinterpret_cast<const i32x2_t*>(sbuf + 2 * kScaleBytesA + (b_row0 + 32 * j + lrow) * kScaleRowBytes + 8 * pair);
+      gw[j] = *reinterpret_cast<const i32x2_t*>(sbuf + F::kScalesA * kScaleBytesA + (b_row0 + 32 * j + lrow) * kScaleRowBytes +
+                                                8 * pair);
   };
 
   f32x16_t acc[kTM][kTN];
@@ -439,9 +524,9 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     wait_vmcnt<0>();
   wait_lgkmcnt0();
   stage_barrier();
-  i32x4_t ax0[kTM], ar0[kTM], bw0[kTN], ax1[kTM], ar1[kTM], bw1[kTN];
+  i32x4_t a0[kSubA][kTM], bw0[kTN], a1[kSubA][kTM], bw1[kTN];
   read_scale_pair(0);
-  read_step(0, 0, ax0, ar0, bw0);
+  read_step(0, 0, a0, bw0);
 
   // One stage; P = st % 4 is a compile-time constant so that every wait count
   // and scale-word index below is one.
@@ -475,8 +560,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     // first MFMA step; meanwhile read the second step's fragments and issue
     // the second part of stage st + 2's loads
     issue_stage(st + kRing - 1, std::integral_constant<int, 1>{});
-    read_step(st, 1, ax1, ar1, bw1);
-    mfma_step<0, kResid, kTM, kTN>(acc, ax0, ar0, bw0, cx, cr, cw);
+    read_step(st, 1, a1, bw1);
+    mfma_step<0, F, kTM, kTN>(acc, a0, bw0, cx, cr, cw);
     interleave_hint<kReadsPerStep, kFast ? kDmaPerStage - kPart0 : 0, kMfmaPerStep>();
 
     // Stage st + 1 must have landed, and at the end of a group also the next
@@ -513,8 +598,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     // these reads fetch values nobody uses.
     if (P == 1) read_scale_pair(1);
     if (P == 3) read_scale_pair(0);
-    read_step(st + 1, 0, ax0, ar0, bw0);
-    mfma_step<1, kResid, kTM, kTN>(acc, ax1, ar1, bw1, cx, cr, cw);
+    read_step(st + 1, 0, a0, bw0);
+    mfma_step<1, F, kTM, kTN>(acc, a1, bw1, cx, cr, cw);
     interleave_hint<kReadsPerStep + (P % 2 == 1 ? kScaleRowReads : 0),
                     kFast ? kPart0 + (P == 2 ? kScaleLoadsPerWave : 0) : 0, kMfmaPerStep>();
     __builtin_amdgcn_sched_barrier(0);
@@ -628,16 +713,15 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     store_tile(cm0, cn0);
 }
 
-template <class C, bool kResid, bool kOutBf16, bool kCanStream>
+template <class C, class F, bool kOutBf16, bool kCanStream>
 hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipStream_t stream) {
   if (p.grid <= 0) return hipSuccess;
   if (kCanStream && stream_tiles)
-    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true, kCanStream>), dim3(p.wg), dim3(64 * C::kWaves), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, F, kOutBf16, true, kCanStream>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
   else if (fast)
-    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, true, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, F, kOutBf16, true, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<C, kResid, kOutBf16, false, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<C, F, kOutBf16, false, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -645,10 +729,12 @@ hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipSt
 // leaves a last partial round that split into quadrants (two quadrant
 // workgroups per CU) finishes sooner, the whole rounds go out as big tiles
 // and the rest as quadrants in a second launch.
-template <bool kResid, bool kOutBf16>
+template <class F, bool kOutBf16>
 hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) {
-  p.gm = BigTile::kBM;
-  p.gn = BigTile::kBN;
+  using Big = typename Tiles<F>::Big;
+  using Quad = typename Tiles<F>::Quad;
+  p.gm = Big::kBM;
+  p.gn = Big::kBN;
   p.tiles_m = (p.M + p.gm - 1) / p.gm;
   p.tiles_n = (p.N + p.gn - 1) / p.gn;
   const int tiles = p.tiles_m * p.tiles_n;
@@ -664,15 +750,15 @@ hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) 
   // When every tile lies inside Y and Y takes vector stores, one workgroup
   // per CU streams its tiles back to back; otherwise every tile gets its own
   // workgroup.
-  const bool stream_tiles = fast && p.vec_out && p.M % BigTile::kBM == 0 && p.N % BigTile::kBN == 0 && big > cus;
+  const bool stream_tiles = fast && p.vec_out && p.M % Big::kBM == 0 && p.N % Big::kBN == 0 && big > cus;
   p.wg = stream_tiles ? cus : big;
-  hipError_t e = launch_tiles<BigTile, kResid, kOutBf16, true>(p, fast, stream_tiles, stream);
+  hipError_t e = launch_tiles<Big, F, kOutBf16, true>(p, fast, stream_tiles, stream);
   if (e != hipSuccess || big == tiles) return e;
   p.first = big;
   p.grid = 4 * (tiles - big);
   p.quadrants = 1;
   p.wg = p.grid;
-  return launch_tiles<QuadTile, kResid, kOutBf16, false>(p, fast, false, stream);
+  return launch_tiles<Quad, F, kOutBf16, false>(p, fast, false, stream);
 }
 
 int cu_count() {
@@ -689,8 +775,8 @@ int cu_count() {
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, const uint8_t* sr,
-                       const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N, int64_t K,
+hipError_t launch_gemm(int x_fmt, int r_fmt, const uint8_t* qx, const uint8_t* sx, const uint8_t* qr,
+                       const uint8_t* sr, const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N, int64_t K,
                        void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
   GemmParams p;
   p.qx = qx; p.sx = sx; p.qr = qr; p.sr = sr; p.w = w; p.sw = sw;
@@ -701,9 +787,14 @@ hipError_t launch_gemm(const uint8_t* qx, const uint8_t* sx, const uint8_t* qr, 
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
   const bool fast = (K % (kBK * kScaleGroup)) == 0;
   const int cus = cu_count();
-  if (qr != nullptr)
-    return y_bf16 ? launch_variant<true, true>(p, fast, cus, stream) : launch_variant<true, false>(p, fast, cus, stream);
-  return y_bf16 ? launch_variant<false, true>(p, fast, cus, stream) : launch_variant<false, false>(p, fast, cus, stream);
+  if (qr == nullptr) r_fmt = 0;
+  switch (x_fmt * 10 + r_fmt) {
+    case 40: return y_bf16 ? launch_variant<FmtW4A4, true>(p, fast, cus, stream) : launch_variant<FmtW4A4, false>(p, fast, cus, stream);
+    case 44: return y_bf16 ? launch_variant<FmtRfq, true>(p, fast, cus, stream) : launch_variant<FmtRfq, false>(p, fast, cus, stream);
+    case 48: return y_bf16 ? launch_variant<FmtRfq8, true>(p, fast, cus, stream) : launch_variant<FmtRfq8, false>(p, fast, cus, stream);
+    case 80: return y_bf16 ? launch_variant<FmtW4A8, true>(p, fast, cus, stream) : launch_variant<FmtW4A8, false>(p, fast, cus, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace rfq

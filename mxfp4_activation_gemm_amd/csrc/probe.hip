@@ -1,6 +1,6 @@
 // MFMA issue ceiling under the power limit (measurement probe, not part of
-// the RFQ layer): a loop of the GEMM's scaled FP4 MFMA on caller-supplied
-// operand bytes, with no memory traffic inside the loop, timed per
+// the RFQ layer): a loop of the GEMM's scaled MFMA (E2M1 x E2M1, or E2M1 x
+// E4M3 as in the MXFP8 activation variants) on caller-supplied operand bytes, with no memory traffic inside the loop, timed per
 // workgroup in shader-clock cycles (s_memtime) and in 100 MHz constant-clock
 // ticks (s_memrealtime), so that both the rate and the clock it ran at can be
 // read back.
@@ -17,15 +17,20 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 512;   // two waves per SIMD, like the GEMM's main tile
 constexpr int kAcc = 8;         // independent accumulators per wave
 
+// kBFmt: format of the second operand, 4 (E2M1, 16 bytes per lane) or 8
+// (E4M3, 32 bytes per lane).
+template <int kBFmt>
 __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a, uint32_t a_n, const i32x4_t* b,
                                                                  uint32_t b_n, int iters, uint64_t* stamps,
                                                                  float* sink) {
   const uint32_t t = threadIdx.x;
-  i32x4_t ra[4], rb[4];
+  i32x4_t ra[4];
+  i32x8_t rb[4];
   for (int i = 0; i < 4; ++i) {
     const uint32_t slot = (blockIdx.x * kThreads + t) * 4 + i;
     ra[i] = a[slot % a_n];
-    rb[i] = b[slot % b_n];
+    const i32x4_t lo = b[(2 * slot) % b_n], hi = b[(2 * slot + 1) % b_n];
+    rb[i] = kBFmt == 8 ? i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w} : i32x8_t{lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
   }
   f32x16_t acc[kAcc];
   for (int q = 0; q < kAcc; ++q)
@@ -36,9 +41,9 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int q = 0; q < kAcc; ++q) {
-        const i32x4_t x = ra[(q + s) & 3], y = rb[(q / 2 + s) & 3];
+        const i32x4_t x = ra[(q + s) & 3];
         acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(i32x8_t{x.x, x.y, x.z, x.w, 0, 0, 0, 0},
-                                                                 i32x8_t{y.x, y.y, y.z, y.w, 0, 0, 0, 0}, acc[q], 4, 4,
+                                                                 rb[(q / 2 + s) & 3], acc[q], 4, kBFmt == 8 ? 0 : 4,
                                                                  0, 120 + q, 0, 122);
       }
   }
@@ -55,11 +60,16 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a
 
 }  // namespace
 
-hipError_t launch_mfma_ceiling(const uint8_t* a, size_t a_bytes, const uint8_t* b, size_t b_bytes, int workgroups,
-                               int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(workgroups), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const i32x4_t*>(a), (uint32_t)(a_bytes / 16), reinterpret_cast<const i32x4_t*>(b),
-                     (uint32_t)(b_bytes / 16), iters, stamps, sink);
+hipError_t launch_mfma_ceiling(const uint8_t* a, size_t a_bytes, const uint8_t* b, size_t b_bytes, int b_fmt,
+                               int workgroups, int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
+  const auto* ap = reinterpret_cast<const i32x4_t*>(a);
+  const auto* bp = reinterpret_cast<const i32x4_t*>(b);
+  if (b_fmt == 8)
+    hipLaunchKernelGGL(mfma_ceiling_kernel<8>, dim3(workgroups), dim3(kThreads), 0, stream, ap, (uint32_t)(a_bytes / 16),
+                       bp, (uint32_t)(b_bytes / 16), iters, stamps, sink);
+  else
+    hipLaunchKernelGGL(mfma_ceiling_kernel<4>, dim3(workgroups), dim3(kThreads), 0, stream, ap, (uint32_t)(a_bytes / 16),
+                       bp, (uint32_t)(b_bytes / 16), iters, stamps, sink);
   return hipGetLastError();
 }
 

@@ -32,7 +32,14 @@
 //    (a + b, a - b). Activations quantize X H; weights W H / 32 (an exact
 //    power of two), so the GEMM returns X W^T unchanged. Codes are decided
 //    on the rotated fp32 values; the residual stays exact (|R| is at most
-//    half an E2M1 step, so R = v - deq(v) loses no bits in fp32).
+//    half an E2M1 step, so R = v - deq(v) loses no bits in fp32);
+//  * MXFP8 output ("Activation Outliers Matter", Abstract and §1 study MXFP8
+//    beside MXFP4; elements per OCP MX v1.0): E4M3 codes, one byte per
+//    element, with se = max(floor(log2 amax) - 8, -127), either for X itself
+//    (W4A8) or for the residual R of an MXFP4 Q(X) (RFQ with an MXFP8 second
+//    path). Values are clamped to +-448 * 2^se before the scaled fp32 -> FP8
+//    conversion (round to nearest even), which is the saturation rule: from
+//    448 up to the 464 midpoint the nearest value is 448 anyway.
 
 #include "kernels.h"
 
@@ -42,7 +49,9 @@ namespace {
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;          // 4 waves per workgroup
 constexpr int kUnits = 4;              // 16-block units per wave
@@ -96,6 +105,49 @@ __device__ __forceinline__ unsigned encode_f32x8(const float* f, float s) {
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[4], f[5], s, 2);
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[6], f[7], s, 3);
   return c;
+}
+
+// E4M3 codes of 8 fp32 values at E8M0 scale code `code` (not 255): byte j of
+// the 8 holds element j. Each value is first clamped to +-448 * 2^se (whose
+// fp32 pattern has exponent field code + 8 and the mantissa of 1.75).
+__device__ __forceinline__ u32x2_t encode_e4m3_f32x8(const float* f, unsigned code) {
+  const float s = scale_operand(code);
+  const float lim = __builtin_bit_cast(float, ((code + 8u) << 23) | 0x00600000u);
+  float c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_fmed3f(f[j], -lim, lim);
+  i16x2_t lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c[0], c[1], s, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c[2], c[3], s, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, c[4], c[5], s, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, c[6], c[7], s, true);
+  return u32x2_t{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
+// The largest element exponent of a format: 2 for E2M1 (6 = 1.5 * 2^2), 8 for
+// E4M3 (448 = 1.75 * 2^8). The block scale code is max(e_amax - emax, 0) for
+// the biased fp32 exponent e_amax of the block maximum.
+template <int kFmt>
+constexpr unsigned kEmax = kFmt == 8 ? 8u : 2u;
+
+// A lane's 8 elements of one block in format kFmt (4: E2M1, 8: E4M3) at scale
+// code `code`: 4 bytes of packed nibbles (in .x) or 8 bytes.
+template <int kFmt>
+__device__ __forceinline__ u32x2_t encode_part(const float* f, unsigned code) {
+  if constexpr (kFmt == 8)
+    return encode_e4m3_f32x8(f, code);
+  else
+    return u32x2_t{encode_f32x8(f, scale_operand(code)), 0u};
+}
+
+// Stores a lane's part of block g (codes of 32 elements: 16 bytes for E2M1,
+// 32 for E4M3, of which this lane holds a quarter).
+template <int kFmt>
+__device__ __forceinline__ void store_part(uint8_t* q, uint32_t g, uint32_t part, u32x2_t c) {
+  if constexpr (kFmt == 8)
+    *reinterpret_cast<u32x2_t*>(q + (uint64_t)g * 32 + part * 8) = c;
+  else
+    *reinterpret_cast<unsigned*>(q + (uint64_t)g * 16 + part * 4) = c.x;
 }
 
 // r[2J], r[2J+1] = x[2J], x[2J+1] minus their decoded codes (byte J of
@@ -158,10 +210,13 @@ struct QuantParams {
   uint32_t total_blocks;  // rows * K / 32
 };
 
-// kF32In: X is fp32 (else bf16). kRotate: 0 none, 1 X H (activations),
-// 2 X H / 32 (weights).
-template <bool kResidual, bool kF32In, int kRotate>
+// kXFmt: format of Q(X), 4 (E2M1) or 8 (E4M3). kRFmt: format of Q(R), 0 for
+// no residual pass (the residual needs an E2M1 Q(X)). kF32In: X is fp32
+// (else bf16). kRotate: 0 none, 1 X H (activations), 2 X H / 32 (weights).
+template <int kXFmt, int kRFmt, bool kF32In, int kRotate>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
+  constexpr bool kResidual = kRFmt != 0;
+  static_assert(kXFmt == 4 || (kXFmt == 8 && !kResidual && kRotate == 0), "format combination");
   const unsigned lane = threadIdx.x & 63;
   const unsigned wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const uint32_t g0 = wave * kBlocksPerWave;   // first block of this wave
@@ -219,34 +274,33 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       e = quad_max_u32(f32x8_absmax_bits(xf)) >> 23;
     }
     const bool nonfinite = e == 255;
-    const unsigned sxc = nonfinite ? 255u : (e > 2 ? e - 2 : 0u);
+    const unsigned sxc = nonfinite ? 255u : (e > kEmax<kXFmt> ? e - kEmax<kXFmt> : 0u);
     const float s = scale_operand(sxc);
-    unsigned cx = encode_f32x8(xf, s);
-    if (nonfinite) cx = 0;
+    u32x2_t cx = encode_part<kXFmt>(xf, sxc);
+    if (nonfinite) cx = u32x2_t{0u, 0u};
 
-    unsigned cr = 0, src = 255u;
-    if (kResidual) {
+    u32x2_t cr = {0u, 0u};
+    unsigned src = 255u;
+    if constexpr (kResidual) {
       // deq(Q(X)) and R = X - deq(Q(X)) in fp32
       float r[8];
-      residual_pair<0>(xf, cx, s, r);
-      residual_pair<1>(xf, cx, s, r);
-      residual_pair<2>(xf, cx, s, r);
-      residual_pair<3>(xf, cx, s, r);
+      residual_pair<0>(xf, cx.x, s, r);
+      residual_pair<1>(xf, cx.x, s, r);
+      residual_pair<2>(xf, cx.x, s, r);
+      residual_pair<3>(xf, cx.x, s, r);
       float m = fmaxf(fmaxf(fmaxf(fabsf(r[0]), fabsf(r[1])), fmaxf(fabsf(r[2]), fabsf(r[3]))),
                       fmaxf(fmaxf(fabsf(r[4]), fabsf(r[5])), fmaxf(fabsf(r[6]), fabsf(r[7]))));
       const unsigned ramax = quad_max_u32(__builtin_bit_cast(unsigned, m));
       const unsigned er = ramax >> 23;                 // fp32 biased exponent
-      const unsigned rc = er > 2 ? er - 2 : 0u;
-      const float sr = scale_operand(rc);
-      cr = encode_f32x8(r, sr);
-      if (nonfinite) cr = 0;
+      const unsigned rc = er > kEmax<kRFmt> ? er - kEmax<kRFmt> : 0u;
+      cr = encode_part<kRFmt>(r, rc);
+      if (nonfinite) cr = u32x2_t{0u, 0u};
       src = nonfinite ? 255u : rc;
     }
 
     if (valid) {
-      const uint64_t cofs = (uint64_t)g * 16 + part * 4;
-      *reinterpret_cast<unsigned*>(p.qx + cofs) = cx;
-      if (kResidual) *reinterpret_cast<unsigned*>(p.qr + cofs) = cr;
+      store_part<kXFmt>(p.qx, g, part, cx);
+      if constexpr (kResidual) store_part<kRFmt>(p.qr, g, part, cr);
       if (part == 0) {
         p.sx[g] = (uint8_t)sxc;
         if (kResidual) p.sr[g] = (uint8_t)src;
@@ -257,8 +311,20 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 
 }  // namespace
 
-hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int64_t rows, int64_t K, int64_t ldx,
-                           uint8_t* qx, uint8_t* sx, uint8_t* qr, uint8_t* sr, hipStream_t stream) {
+namespace {
+
+template <int kXFmt, int kRFmt, int kRotate>
+void launch_one(bool x_f32, dim3 grid, dim3 block, hipStream_t stream, const QuantParams& p) {
+  if (x_f32)
+    hipLaunchKernelGGL((quantize_kernel<kXFmt, kRFmt, true, kRotate>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((quantize_kernel<kXFmt, kRFmt, false, kRotate>), grid, block, 0, stream, p);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int x_fmt, int r_fmt, int64_t rows, int64_t K,
+                           int64_t ldx, uint8_t* qx, uint8_t* sx, uint8_t* qr, uint8_t* sr, hipStream_t stream) {
   QuantParams p;
   p.x = x;
   p.ldx = ldx;
@@ -271,24 +337,18 @@ hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int64_t rows, 
   const uint64_t waves = (p.total_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
   const uint64_t groups = (waves + kThreads / 64 - 1) / (kThreads / 64);
   const dim3 grid((unsigned)groups), block(kThreads);
-  const bool resid = qr != nullptr;
-  // rotate 1 goes with the residual pass (activations), rotate 2 without it (weights)
-  if (rotate == 1 && resid) {
-    if (x_f32) hipLaunchKernelGGL((quantize_kernel<true, true, 1>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((quantize_kernel<true, false, 1>), grid, block, 0, stream, p);
-  } else if (rotate == 2 && !resid) {
-    if (x_f32) hipLaunchKernelGGL((quantize_kernel<false, true, 2>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((quantize_kernel<false, false, 2>), grid, block, 0, stream, p);
-  } else if (rotate == 0) {
-    if (resid) {
-      if (x_f32) hipLaunchKernelGGL((quantize_kernel<true, true, 0>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((quantize_kernel<true, false, 0>), grid, block, 0, stream, p);
-    } else {
-      if (x_f32) hipLaunchKernelGGL((quantize_kernel<false, true, 0>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((quantize_kernel<false, false, 0>), grid, block, 0, stream, p);
-    }
-  } else {
-    return hipErrorInvalidValue;
+  if (qr == nullptr) r_fmt = 0;
+  // rotation 1 goes with the E2M1 residual pass (activations), rotation 2
+  // with plain E2M1 (weights); E4M3 output only without rotation
+  const int key = rotate * 100 + x_fmt * 10 + r_fmt;
+  switch (key) {
+    case 40: launch_one<4, 0, 0>(x_f32, grid, block, stream, p); break;
+    case 44: launch_one<4, 4, 0>(x_f32, grid, block, stream, p); break;
+    case 48: launch_one<4, 8, 0>(x_f32, grid, block, stream, p); break;
+    case 80: launch_one<8, 0, 0>(x_f32, grid, block, stream, p); break;
+    case 144: launch_one<4, 4, 1>(x_f32, grid, block, stream, p); break;
+    case 240: launch_one<4, 0, 2>(x_f32, grid, block, stream, p); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

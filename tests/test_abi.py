@@ -36,11 +36,11 @@ def declared_functions():
 
 def test_header_declarations_are_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
-    assert lib.rfq_abi_version() == 2
+    assert lib.rfq_abi_version() == 3
 
 
 def status_name(st):
@@ -127,9 +127,10 @@ def test_status_strings(lib):
     assert lib.rfq_status_string(99) == b"unknown status"
 
 
-def test_probe_validation(lib):
+@pytest.mark.parametrize("name", ["rfq_probe_mfma_ceiling", "rfq_probe_mfma_ceiling_e4m3"])
+def test_probe_validation(lib, name):
     def pr(a=FAKE, an=4096, b=FAKE, bn=4096, wg=4, it=10, st=FAKE, sink=FAKE):
-        return status_name(lib.rfq_probe_mfma_ceiling(a, an, b, bn, wg, it, st, sink, None))
+        return status_name(getattr(lib, name)(a, an, b, bn, wg, it, st, sink, None))
     assert pr(a=None) == "RFQ_ERR_NULL_POINTER"
     assert pr(sink=None) == "RFQ_ERR_NULL_POINTER"
     assert pr(a=FAKE + 8) == "RFQ_ERR_MISALIGNED"
@@ -149,3 +150,29 @@ def test_rotated_quantize_validation(lib):
     assert status_name(w(FAKE + 4, 1, 4, 64, 64, FAKE, FAKE, None)) == "RFQ_ERR_MISALIGNED"
     assert status_name(w(FAKE, 0, 4, 64, 64, None, FAKE, None)) == "RFQ_ERR_NULL_POINTER"
     assert status_name(w(None, 0, 0, 64, 64, None, None, None)) == "RFQ_OK"
+
+
+def test_mxfp8_entry_points_validation(lib):
+    q8, r8 = lib.rfq_quantize_mxfp8, lib.rfq_residual_quantize_mxfp8
+    assert status_name(q8(None, 0, 4, 64, 64, FAKE, FAKE, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(q8(FAKE, 2, 4, 64, 64, FAKE, FAKE, None)) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert status_name(q8(FAKE, 0, 4, 80, 80, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_SHAPE"
+    assert status_name(q8(FAKE, 0, 4, 64, 64, FAKE + 8, FAKE, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(q8(None, 0, 0, 64, 64, None, None, None)) == "RFQ_OK"
+    assert status_name(r8(FAKE, 0, 4, 64, 64, FAKE, FAKE, FAKE, None, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(r8(FAKE, 1, 4, 64, 66, FAKE, FAKE, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_STRIDE"
+    assert status_name(r8(FAKE, 0, 4, 64, 64, FAKE, FAKE, FAKE + 4, FAKE, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(r8(None, 0, 0, 64, 64, None, None, None, None, None)) == "RFQ_OK"
+
+    g8, gr8 = lib.rfq_gemm_w4a8, lib.rfq_gemm_w4a4_mxfp8_residual
+    assert status_name(g8(None, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 0, 8, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(g8(FAKE, FAKE, FAKE, FAKE, 8, 8, 40, FAKE, 0, 8, None)) == "RFQ_ERR_INVALID_SHAPE"
+    assert status_name(g8(FAKE, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 3, 8, None)) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert status_name(g8(FAKE, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 0, 4, None)) == "RFQ_ERR_INVALID_STRIDE"
+    assert status_name(g8(FAKE + 8, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 0, 8, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(g8(None, None, None, None, 0, 8, 64, None, 0, 8, None)) == "RFQ_OK"
+    assert status_name(gr8(FAKE, FAKE, None, None, FAKE, FAKE, 8, 8, 64, FAKE, 0, 8, None)) == \
+        "RFQ_ERR_NULL_POINTER"                                     # the residual term is required here
+    assert status_name(gr8(FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 0, 8, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(gr8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 64, FAKE + 1, 1, 8, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(gr8(None, None, None, None, None, None, 8, 0, 64, None, 0, 8, None)) == "RFQ_OK"

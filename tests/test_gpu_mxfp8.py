@@ -1,0 +1,319 @@
+"""GPU parity of the MXFP8 (E4M3) variants against the oracle: MXFP8
+quantization and the RFQ encoding with an MXFP8 residual bit-exact (codes and
+scales), and the W4A8 and MXFP8-residual GEMMs within the per-output
+tolerance: 1e-5 of the condition scale, plus the bound on the E4M3 MFMA's own
+group truncation (gpu_helpers.e4m3_group_bound; pinned exactly below through
+the GEMM entry point), plus the bf16 half-ulp for bf16 Y."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_activation_gemm_amd as rfq
+import oracle
+import workloads
+from gpu_helpers import assert_bytes_equal, check_y, dev_bf16, dev_u8, e4m3_group_bound, host, host_bf16_as_f64, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rfq.library()
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def y_host(y):
+    return host_bf16_as_f64(y) if y.dtype == torch.bfloat16 else host(y).astype(np.float64)
+
+
+def near_e4m3_midpoints(rng, rows, K):
+    """fp32 blocks that pin every E4M3 rounding decision: the first element of
+    a block (511, which saturates) fixes the scale, the others sit at
+    midpoints between neighbouring E4M3 values (subnormal range, 448/464/480
+    and saturation included) and up to 3 float32 ulps either side, with
+    random signs, positions and block scale exponents."""
+    mags = oracle.E4M3_MAGNITUDES
+    mids = np.concatenate([(mags[:-1] + mags[1:]) / 2, mags, [450.0, 464.0, 470.0, 480.0, 500.0, 511.0]])
+    v = rng.choice(mids, size=(rows, K)).astype(np.float32)
+    k = rng.integers(-3, 4, size=(rows, K))
+    for step in range(3):
+        v = np.where(k > step, np.nextafter(v, np.float32(np.inf)), v)
+        v = np.where(k < -step, np.nextafter(v, np.float32(0)), v)
+    v = np.minimum(v, np.float32(511.0))
+    v[:, ::32] = 511.0
+    v *= rng.choice([-1.0, 1.0], size=(rows, K)).astype(np.float32)
+    se = rng.integers(-100, 100, size=(rows, K // 32))
+    return (v * np.repeat(np.exp2(se), 32, axis=1)).astype(np.float32)
+
+
+def spiky_bf16(rng, rows, K):
+    x = rng.laplace(0, 1, size=(rows, K)).astype(np.float32)
+    x[:, rng.choice(K, size=8, replace=False)] *= 80.0
+    x[2, 5] = 3e38
+    x[6, :32] *= 1e-36                          # a block near the bottom of the scale range
+    bits = workloads.f32_to_bf16_bits(x)
+    bits[3, 40] = 0x7FC0          # NaN
+    bits[4, 70] = 0xFF80          # -Inf
+    bits[5, :32] = 0x8000         # -0.0 block
+    bits[7, 64:96] = 0x0001       # bf16 subnormals
+    return bits
+
+
+def inputs(kind, rng, rows, K):
+    """(device tensor, float64 values) of a test activation."""
+    if kind == "bf16":
+        b = spiky_bf16(rng, rows, K)
+        return dev_bf16(b), oracle.bf16_bits_to_f64(b)
+    if kind == "fp32_midpoints":
+        x = near_e4m3_midpoints(rng, rows, K)
+    else:
+        x = (rng.standard_t(3, size=(rows, K)) * np.exp(rng.uniform(-8, 8, size=(rows, 1)))).astype(np.float32)
+        x[0, :32] = np.float32(1e-40)
+        x[1, 3] = np.inf
+    return dev_f32(x), x.astype(np.float64)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp32_midpoints", "fp32_heavy"])
+def test_quantize_mxfp8_bit_exact(kind):
+    rng = np.random.default_rng({"bf16": 51, "fp32_midpoints": 52, "fp32_heavy": 53}[kind])
+    rows, K = 136, 1024
+    xd, x64 = inputs(kind, rng, rows, K)
+    log(f"[mxfp8] quantize {kind}")
+    codes, scales = rfq.quantize_mxfp8(xd)
+    torch.cuda.synchronize()
+    wc, ws = oracle.quantize_mxfp8(x64)
+    assert_bytes_equal(host(scales), ws, f"{kind} scales")
+    assert_bytes_equal(host(codes), wc, f"{kind} codes")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp32_midpoints", "fp32_heavy"])
+def test_residual_quantize_mxfp8_bit_exact(kind):
+    rng = np.random.default_rng({"bf16": 61, "fp32_midpoints": 62, "fp32_heavy": 63}[kind])
+    rows, K = 136, 1024
+    xd, x64 = inputs(kind, rng, rows, K)
+    log(f"[mxfp8] residual quantize {kind}")
+    qx, sx, qr8, sr = rfq.residual_quantize_mxfp8(xd)
+    torch.cuda.synchronize()
+    oqx, osx, oqr8, osr = oracle.residual_quantize_fp8(x64)
+    assert_bytes_equal(host(sx), osx, f"{kind} SX")
+    assert_bytes_equal(host(qx), oracle.pack_codes(oqx), f"{kind} Q(X)")
+    assert_bytes_equal(host(sr), osr, f"{kind} SR")
+    assert_bytes_equal(host(qr8), oqr8, f"{kind} Q8(R)")
+
+
+def heavy_bf16(rng, rows, K, outliers=3):
+    x = rng.standard_t(3, size=(rows, K)).astype(np.float32)
+    if outliers:
+        x[:, rng.choice(K, size=min(outliers, K), replace=False)] *= 60
+    return workloads.f32_to_bf16_bits(x)
+
+
+def run_variant(variant, x, w):
+    """GPU quantize + GEMM of one variant (fp32 Y and bf16 Y share the codes)."""
+    wq, sw = rfq.quantize_mxfp4(w)
+    if variant == "w4a8":
+        qx8, sx = rfq.quantize_mxfp8(x)
+        return lambda od: rfq.gemm_w4a8(qx8, sx, wq, sw, out_dtype=od)
+    qx, sx, qr8, sr = rfq.residual_quantize_mxfp8(x)
+    return lambda od: rfq.gemm_w4a4_mxfp8_residual(qx, sx, qr8, sr, wq, sw, out_dtype=od)
+
+
+def oracle_variant(variant, x64, w64):
+    """(Y, S, bound on the E4M3 instruction's truncation) from the oracle's
+    encodings; only the E4M3 term (X8, or R8) is truncated by the MFMA."""
+    if variant == "w4a8":
+        y, s, (qx8, sx), (wq, sw) = oracle.linear_w4a8(x64, w64)
+        a8 = oracle.dequantize_mxfp8(qx8, sx)
+    else:
+        y, s, (_, _, qr8, sr), (wq, sw) = oracle.linear_fp8_residual(x64, w64)
+        a8 = oracle.dequantize_mxfp8(qr8, sr)
+    return y, s, e4m3_group_bound(a8, oracle.dequantize(wq, sw))
+
+
+VARIANTS = ["w4a8", "fp8_residual"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("M,N,K", [(300, 520, 416), (1, 1, 32), (33, 65, 96), (257, 255, 128), (70, 300, 4128),
+                                   (512, 512, 1024), (130, 260, 512)])
+def test_gemm_every_output(variant, M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 13 + K + len(variant))
+    xb, wb = heavy_bf16(rng, M, K), workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[mxfp8] {variant} M={M} N={N} K={K}")
+    gemm = run_variant(variant, dev_bf16(xb), dev_bf16(wb))
+    y_ref, s_ref, hw = oracle_variant(variant, oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb))
+    for od in (torch.float32, torch.bfloat16):
+        check_y(y_host(gemm(od)), y_ref, s_ref, od, f"{variant} {M}x{N}x{K} {od}", extra=hw)
+
+
+def test_all_e4m3_by_e2m1_code_pairs():
+    """Row a of QX8 holds E4M3 code a at k = 9 (the 254 non-NaN codes), row b
+    of W holds E2M1 code b there; unit scales: Y[a, b] = value(a) value(b)."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    qx8 = np.zeros((len(codes), 32), np.uint8)
+    qx8[:, 9] = codes
+    wq = np.zeros((16, 32), np.uint8)
+    wq[:, 9] = np.arange(16)
+    log("[mxfp8] E4M3 x E2M1 code pairs")
+    y = rfq.gemm_w4a8(dev_u8(qx8), dev_u8(np.full((len(codes), 1), 127, np.uint8)), dev_u8(oracle.pack_codes(wq)),
+                      dev_u8(np.full((16, 1), 127, np.uint8)), out_dtype=torch.float32)
+    a = np.array([oracle.e4m3_value(c) for c in codes])
+    b = np.array([oracle.e2m1_value(c) for c in range(16)])
+    assert (host(y).astype(np.float64) == np.outer(a, b)).all()
+
+
+def test_e4m3_group_truncation():
+    """The E4M3 instruction's arithmetic that the tolerances account for.
+    Two-term rows (unit scales, E2M1 weight 1.0): a large value 2^E at k = 0
+    and a small one m 2^-9 (either sign) at k = 1 (same group of 8) or k = 8
+    (next group). In the same group the small product comes back truncated
+    toward zero to a multiple of 2^(E - 13); in another group it is kept.
+    Then rows with a large code in every group, small codes of mixed signs
+    around it and a mixed E2M1 weight row: Y misses the exact sum on most
+    rows, always within the bound the tolerances use."""
+    rows, want = [], []
+    for E in range(4, 9):
+        for m in range(1, 8):
+            for sgn in (1, -1):
+                for k in (1, 8):
+                    q = np.zeros(64, np.uint8)
+                    q[0] = 0x38 + (E << 3)                          # 2^E
+                    q[k] = m | (0x80 if sgn < 0 else 0)             # m * 2^-9 (subnormal codes)
+                    ulp = 2.0 ** (E - 13)
+                    small = sgn * m * 2.0 ** -9
+                    kept = np.trunc(small / ulp) * ulp if k == 1 else small
+                    rows.append(q)
+                    want.append(2.0 ** E + kept)
+    qa = np.array(rows)
+    n = len(rows)
+    wq = np.full((1, 64), 2, np.uint8)                              # 1.0 everywhere
+    ones = lambda r: np.full((r, 2), 127, np.uint8)
+    log("[mxfp8] E4M3 MFMA group truncation")
+    y = host(rfq.gemm_w4a8(dev_u8(qa), dev_u8(ones(n)), dev_u8(oracle.pack_codes(wq)), dev_u8(ones(1)),
+                           out_dtype=torch.float32))[:, 0].astype(np.float64)
+    assert (y == np.array(want)).all(), np.argwhere(y != np.array(want))[:5].ravel().tolist()
+
+    rng = np.random.default_rng(99)
+    cases = 48
+    qx8 = np.zeros((cases, 64), np.uint8)
+    for c in range(cases):
+        small = rng.integers(0x01, 0x20, size=64)                  # 2^-9 .. < 2^-3
+        sign = (rng.random(64) < 0.3).astype(np.uint8) << 7
+        qx8[c] = (small | sign).astype(np.uint8)
+        for g in range(8):
+            qx8[c, 8 * g + rng.integers(0, 8)] = rng.integers(0x50, 0x7F) | (0x80 if rng.random() < 0.3 else 0)
+    wq = rng.integers(1, 8, size=(1, 64)).astype(np.uint8) | ((rng.random((1, 64)) < 0.3).astype(np.uint8) << 3)
+    y = host(rfq.gemm_w4a8(dev_u8(qx8), dev_u8(ones(cases)), dev_u8(oracle.pack_codes(wq)), dev_u8(ones(1)),
+                           out_dtype=torch.float32))[:, 0].astype(np.float64)
+    a = oracle.dequantize_mxfp8(qx8, ones(cases))
+    w = oracle.dequantize(wq, ones(1))[0]
+    exact = a @ w
+    fp32 = 4 * 2.0 ** -24 * (np.abs(a) @ np.abs(w))
+    assert (np.abs(y - exact) > fp32).sum() > cases // 2
+    assert (np.abs(y - exact) <= e4m3_group_bound(a, w[None, :])[:, 0] + fp32).all()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_random_codes_and_scales_every_lane_position(variant):
+    rng = np.random.default_rng(71 + len(variant))
+    M, N, K = 96, 160, 640
+    fin8 = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    wq = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    sw = rng.integers(64, 170, (N, K // 32)).astype(np.uint8)
+    sx = rng.integers(64, 170, (M, K // 32)).astype(np.uint8)
+    log(f"[mxfp8] random codes {variant}")
+    if variant == "w4a8":
+        qx8 = rng.choice(fin8, size=(M, K))
+        y = rfq.gemm_w4a8(dev_u8(qx8), dev_u8(sx), dev_u8(oracle.pack_codes(wq)), dev_u8(sw), out_dtype=torch.float32)
+        y_ref, s_ref = oracle.gemm_w4a8(qx8, sx, wq, sw)
+        hw = e4m3_group_bound(oracle.dequantize_mxfp8(qx8, sx), oracle.dequantize(wq, sw))
+    else:
+        qx = rng.integers(0, 16, (M, K)).astype(np.uint8)
+        qr8 = rng.choice(fin8, size=(M, K))
+        sr = rng.integers(64, 170, (M, K // 32)).astype(np.uint8)
+        y = rfq.gemm_w4a4_mxfp8_residual(dev_u8(oracle.pack_codes(qx)), dev_u8(sx), dev_u8(qr8), dev_u8(sr),
+                                         dev_u8(oracle.pack_codes(wq)), dev_u8(sw), out_dtype=torch.float32)
+        y_ref, s_ref = oracle.gemm_w4a4_fp8_residual(qx, sx, qr8, sr, wq, sw)
+        hw = e4m3_group_bound(oracle.dequantize_mxfp8(qr8, sr), oracle.dequantize(wq, sw))
+    check_y(host(y), y_ref, s_ref, torch.float32, f"random codes {variant}", extra=hw)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_nan_block_gives_nan_outputs_only_in_its_row(variant):
+    rng = np.random.default_rng(81)
+    M, N, K = 64, 96, 256
+    xb = heavy_bf16(rng, M, K)
+    xb[5, 40] = 0x7FC0
+    xb[9, 200] = 0x7F80
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[mxfp8] NaN/Inf blocks {variant}")
+    y = host(run_variant(variant, dev_bf16(xb), dev_bf16(wb))(torch.float32))
+    assert np.isnan(y[5]).all() and np.isnan(y[9]).all()
+    assert np.isfinite(y[[r for r in range(M) if r not in (5, 9)]]).all()
+
+
+@pytest.mark.parametrize("variant,M,N,K", [("w4a8", 4096, 8192, 512), ("fp8_residual", 4096, 4096, 512),
+                                           ("fp8_residual", 2048, 4096, 1024)])
+def test_streamed_tiles_every_output(variant, M, N, K):
+    """Two whole rounds of main tiles on 256 CUs (256 x 256 for W4A8, 128 x 256
+    for the MXFP8 residual): each workgroup streams its tiles back to back.
+    Every output checked (bf16 Y)."""
+    rng = np.random.default_rng(M + N + K + 91)
+    xb = heavy_bf16(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[mxfp8] streamed {variant} M={M} N={N} K={K}")
+    y = y_host(run_variant(variant, dev_bf16(xb), dev_bf16(wb))(torch.bfloat16))
+    y_ref, s_ref, hw = oracle_variant(variant, oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb))
+    check_y(y, y_ref, s_ref, torch.bfloat16, f"streamed {variant}", extra=hw)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_two_launch_split_sampled(variant):
+    """A tile count that leaves a partial last round (main tiles, then
+    quadrants), partial edge tiles in both; sampled rows x columns."""
+    rng = np.random.default_rng(95)
+    M, N, K = 4100, 4200, 1024
+    xb = heavy_bf16(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[mxfp8] two-launch split {variant}")
+    y = host(run_variant(variant, dev_bf16(xb), dev_bf16(wb))(torch.float32))
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, 256, M - 1, M - 4], rng.choice(M, 57, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, N - 1, N - 100], rng.choice(N, 57, replace=False)]))
+    y_ref, s_ref, hw = oracle_variant(variant, oracle.bf16_bits_to_f64(xb[rows]), oracle.bf16_bits_to_f64(wb[cols]))
+    check_y(y[np.ix_(rows, cols)], y_ref, s_ref, torch.float32, f"split {variant}", extra=hw)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_full_size_sampled(variant):
+    """The Wan2.2-style FFN layer at full size, as the benchmark's variant
+    lines run it; sampled rows of the codes bit-exact, sampled outputs."""
+    cfg = workloads.CONFIGS["wan22_ffn"]
+    log(f"[mxfp8] full size {variant} {cfg.name}")
+    xb, wb = workloads.x_bf16(cfg), workloads.w_bf16(cfg)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    wq, sw = rfq.quantize_mxfp4(w)
+    rows = workloads.sample_rows(cfg, n_random=62)
+    cols = np.unique(np.concatenate([[0, cfg.N - 1], np.random.default_rng(cfg.seed).choice(cfg.N, 126, replace=False)]))
+    x64 = oracle.bf16_bits_to_f64(xb[rows])
+    ri = torch.from_numpy(rows).cuda()
+    if variant == "w4a8":
+        qx8, sx = rfq.quantize_mxfp8(x)
+        y = rfq.gemm_w4a8(qx8, sx, wq, sw, out_dtype=torch.bfloat16)
+        oc, osc = oracle.quantize_mxfp8(x64)
+        assert_bytes_equal(host(qx8[ri]), oc, "QX8 rows")
+        assert_bytes_equal(host(sx[ri]), osc, "SX rows")
+    else:
+        qx, sx, qr8, sr = rfq.residual_quantize_mxfp8(x)
+        y = rfq.gemm_w4a4_mxfp8_residual(qx, sx, qr8, sr, wq, sw, out_dtype=torch.bfloat16)
+        oqx, osx, oqr8, osr = oracle.residual_quantize_fp8(x64)
+        assert_bytes_equal(host(qx[ri]), oracle.pack_codes(oqx), "QX rows")
+        assert_bytes_equal(host(qr8[ri]), oqr8, "QR8 rows")
+        assert_bytes_equal(host(sr[ri]), osr, "SR rows")
+    torch.cuda.synchronize()
+    y_ref, s_ref, hw = oracle_variant(variant, x64, oracle.bf16_bits_to_f64(wb[cols]))
+    worst = check_y(host_bf16_as_f64(y)[np.ix_(rows, cols)], y_ref, s_ref, torch.bfloat16, f"full {variant}", extra=hw)
+    log(f"   ok, max |dY|/S = {worst:.2e}")
