@@ -13,7 +13,10 @@ with 8 outlier channels x80), W [13824, 5120] quantized to MXFP4, Y bf16.
 Prints one JSON line (rank 0) with the effective TFLOP/s of the step
 (4 M N K per step: the contraction over the doubled K), the per-kernel
 rooflines measured with HIP events on the launch stream, and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload. Beside the layer it times,
+on the same X and weight: the block-Hadamard-rotated quantize pass, the
+plain W4A4 GEMM, and the MXFP8 variants (W4A8; RFQ with an MXFP8 residual),
+each with its own quantize pass.
 """
 import argparse
 import hashlib
@@ -27,9 +30,12 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 / MXFP8 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "RFQ W4A4 linear effective TFLOP/s (% MXFP4 peak); quantize GB/s (% HBM)"
 QUANT_BYTES_PER_ELEM = 2 + 2 * (0.5 + 1.0 / 32)      # bf16 in, Q(X) and Q(R) codes + scales out
+QUANT8_BYTES_PER_ELEM = 2 + 1 + 1.0 / 32              # bf16 in, MXFP8 codes + scales out
+QUANT_R8_BYTES_PER_ELEM = 2 + (0.5 + 1.0 / 32) + (1 + 1.0 / 32)   # bf16 in, Q4(X), Q8(R) out
 CPU_GEMM_ROWS = 4096                                  # rows of X in the oracle GEMM sample
 
 
@@ -111,21 +117,30 @@ def cpu_baseline(cfg):
     }
 
 
-def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5):
+def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=None):
     """The power-limited ceiling of the GEMM's instruction on this workload's
     own operand bytes: rfq_probe_mfma_ceiling runs only scaled FP4 MFMAs (no
     memory traffic in the loop), one 8-wave workgroup per CU; the A operands
-    interleave Q(X) and Q(R) codes, the B operands are weight codes."""
+    interleave Q(X) and Q(R) codes, the B operands are weight codes. With
+    `e4m3` (MXFP8 activation codes) it times the E2M1 x E4M3 instruction of
+    the W4A8 GEMM instead (rfq_probe_mfma_ceiling_e4m3: weight codes first,
+    E4M3 codes second)."""
     lib = rfq.library()
     props = torch.cuda.get_device_properties(0)
     wgs = props.multi_processor_count
-    n = min(qx.numel(), qr.numel(), wq.numel(), 1 << 23) // 32 * 16
-    a = torch.stack([qx.view(-1)[:n].view(-1, 16), qr.view(-1)[:n].view(-1, 16)], 1).reshape(-1).contiguous()
-    b = wq.view(-1)[:2 * n].contiguous()
+    if e4m3 is None:
+        n = min(qx.numel(), qr.numel(), wq.numel(), 1 << 23) // 32 * 16
+        a = torch.stack([qx.view(-1)[:n].view(-1, 16), qr.view(-1)[:n].view(-1, 16)], 1).reshape(-1).contiguous()
+        b = wq.view(-1)[:2 * n].contiguous()
+        fn = lib.rfq_probe_mfma_ceiling
+    else:
+        a = wq.view(-1)[:1 << 22].contiguous()
+        b = e4m3.view(-1)[:1 << 23].contiguous()
+        fn = lib.rfq_probe_mfma_ceiling_e4m3
     stamps = torch.zeros(2 * wgs, dtype=torch.int64, device=qx.device)
     sink = torch.empty(512 * wgs, dtype=torch.float32, device=qx.device)
-    call = lambda: rfq._lib.check(lib.rfq_probe_mfma_ceiling(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), wgs,
-                                                             iters, stamps.data_ptr(), sink.data_ptr(), sp))
+    call = lambda: rfq._lib.check(fn(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), wgs, iters, stamps.data_ptr(),
+                                     sink.data_ptr(), sp))
     call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -138,6 +153,11 @@ def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5):
     st = stamps.cpu().numpy().reshape(-1, 2).astype(np.float64)
     clock = float(np.median(st[:, 0] / (st[:, 1] * 10.0)))      # cycles per 100 MHz tick -> GHz
     tf = flops / (ms * 1e-3) / 1e12
+    if e4m3 is not None:
+        return {"TFLOP_per_s": round(tf, 1), "pct_of_datasheet_fp8_peak": round(100 * tf / FP8_PEAK_TFLOPS, 2),
+                "shader_clock_GHz": round(clock, 3),
+                "what": "scaled E2M1 x E4M3 MFMA loop on this workload's W and MXFP8 X codes, no memory traffic, "
+                        "one 8-wave workgroup per CU (rfq_probe_mfma_ceiling_e4m3)"}
     return {"TFLOP_per_s": round(tf, 1), "pct_of_datasheet_peak": round(100 * tf / FP4_PEAK_TFLOPS, 2),
             "shader_clock_GHz": round(clock, 3),
             "what": "scaled FP4 MFMA loop on this workload's Q(X)/Q(R) and W codes, no memory traffic, "
@@ -238,6 +258,34 @@ def main():
 
     ceiling = mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp)
 
+    # MXFP8 variants on the same layer: W4A8 (X in MXFP8) and RFQ whose
+    # second path quantizes R to MXFP8; the weight stays MXFP4
+    qx8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    qr8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+
+    def quantize8():
+        rfq._lib.check(lib.rfq_quantize_mxfp8(x.data_ptr(), 0, M, K, x.stride(0), qx8.data_ptr(), sx.data_ptr(), sp))
+
+    def quantize_r8():
+        rfq._lib.check(lib.rfq_residual_quantize_mxfp8(x.data_ptr(), 0, M, K, x.stride(0), qx.data_ptr(),
+                                                       sx.data_ptr(), qr8.data_ptr(), sr.data_ptr(), sp))
+    q8_ms = batch_ms(quantize8, 100)
+    qr8_ms = batch_ms(quantize_r8, 100)
+    quantize8()
+    w4a8_ms = batch_ms(lambda: rfq._lib.check(lib.rfq_gemm_w4a8(
+        qx8.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(), rfq._lib.DTYPE_BF16, N,
+        sp)), 50)
+    ceiling8 = mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, e4m3=qx8)
+    quantize_r8()
+    rfq8_ms = batch_ms(lambda: rfq._lib.check(lib.rfq_gemm_w4a4_mxfp8_residual(
+        qx.data_ptr(), sx.data_ptr(), qr8.data_ptr(), sr.data_ptr(), wq.data_ptr(), sw.data_ptr(), M, N, K,
+        y.data_ptr(), rfq._lib.DTYPE_BF16, N, sp)), 50)
+    w4a8_tf = 2.0 * M * N * K / (w4a8_ms * 1e-3) / 1e12
+    # instruction time of the MXFP8-residual GEMM in E2M1-MFMA units: one
+    # E2M1 x E2M1 MFMA per X term, one E2M1 x E4M3 (twice the cycles) per R term
+    rfq8_tf = 4.0 * M * N * K / (rfq8_ms * 1e-3) / 1e12
+    del qx8, qr8
+
     kernel_hash = source_hash("gemm.hip")
     traffic = counter_traffic(args.workload, kernel_hash)
     out = {
@@ -290,6 +338,33 @@ def main():
                 "avg_launch_us": round(gemm_ms * 1e3, 2),
                 "TFLOP_per_s": round(gemm_tflops, 1),
                 "pct_fp4_peak": round(100 * gemm_tflops / FP4_PEAK_TFLOPS, 2),
+            },
+            "quantize_mxfp8": {
+                "avg_launch_us": round(q8_ms * 1e3, 2),
+                "GB_per_s": round(QUANT8_BYTES_PER_ELEM * M * K / (q8_ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * QUANT8_BYTES_PER_ELEM * M * K / (q8_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "algorithmic_bytes": QUANT8_BYTES_PER_ELEM * M * K,
+                "what": "X to MXFP8 (E4M3) for W4A8 (rfq_quantize_mxfp8)",
+            },
+            "quantize_residual_mxfp8": {
+                "avg_launch_us": round(qr8_ms * 1e3, 2),
+                "GB_per_s": round(QUANT_R8_BYTES_PER_ELEM * M * K / (qr8_ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * QUANT_R8_BYTES_PER_ELEM * M * K / (qr8_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "algorithmic_bytes": QUANT_R8_BYTES_PER_ELEM * M * K,
+                "what": "Q4(X) and the residual to MXFP8 (rfq_residual_quantize_mxfp8)",
+            },
+            "gemm_w4a8": {
+                "avg_launch_us": round(w4a8_ms * 1e3, 2),
+                "TFLOP_per_s_2MNK": round(w4a8_tf, 1),
+                "pct_fp8_peak": round(100 * w4a8_tf / FP8_PEAK_TFLOPS, 2),
+                "measured_mfma_ceiling": dict(ceiling8, frac_of_ceiling=round(w4a8_tf / ceiling8["TFLOP_per_s"], 4)),
+            },
+            "gemm_rfq_mxfp8_residual": {
+                "avg_launch_us": round(rfq8_ms * 1e3, 2),
+                "TFLOP_per_s_4MNK": round(rfq8_tf, 1),
+                "over_rfq_time": round(rfq8_ms / gemm_ms, 3),
+                "note": "128 x 256 tiles; per output tile the E2M1 x E4M3 residual MFMAs take twice the cycles of the "
+                        "E2M1 ones, so the instruction-time floor is 1.5x the RFQ GEMM's",
             },
             "gemm_plain_w4a4": {
                 "avg_launch_us": round(w4a4_ms * 1e3, 2),
