@@ -50,6 +50,8 @@ def parse():
                     help="skip the extra quantize measurement on the long-sequence layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the per-configuration layer timings (the other four shapes)")
     return ap.parse_args()
 
 
@@ -164,6 +166,47 @@ def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=No
                     "one 8-wave workgroup per CU (rfq_probe_mfma_ceiling)"}
 
 
+def layer_timings(rfq, torch, cfg, x, wq, sw, batch_ms, reps):
+    """Quantize pass, GEMM and the whole step (both, back to back) of one
+    configuration's layer, each averaged over `reps` back-to-back launches
+    between two events on the launch stream."""
+    M, N, K = cfg.M, cfg.N, cfg.K
+    dev = x.device
+    lib = rfq.library()
+    sp = rfq._stream()
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    qr = torch.empty_like(qx)
+    sx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    sr = torch.empty_like(sx)
+    yd = rfq._lib.DTYPE_FP32 if cfg.y_dtype == "fp32" else rfq._lib.DTYPE_BF16
+    y = torch.empty((M, N), dtype=torch.float32 if cfg.y_dtype == "fp32" else torch.bfloat16, device=dev)
+
+    def quantize():
+        rfq._lib.check(lib.rfq_residual_quantize(x.data_ptr(), 0, M, K, x.stride(0), qx.data_ptr(), sx.data_ptr(),
+                                                 qr.data_ptr(), sr.data_ptr(), sp))
+
+    def gemm():
+        rfq._lib.check(lib.rfq_gemm_w4a4(qx.data_ptr(), sx.data_ptr(), qr.data_ptr(), sr.data_ptr(), wq.data_ptr(),
+                                         sw.data_ptr(), M, N, K, y.data_ptr(), yd, N, sp))
+
+    def step():
+        quantize()
+        gemm()
+    q_ms, g_ms, s_ms = batch_ms(quantize, reps), batch_ms(gemm, reps), batch_ms(step, reps)
+    flops = 4.0 * M * N * K
+    return {
+        "M": M, "K": K, "N": N, "y_dtype": cfg.y_dtype,
+        "step_us": round(s_ms * 1e3, 2),
+        "step_TFLOP_per_s": round(flops / (s_ms * 1e-3) / 1e12, 1),
+        "gemm_us": round(g_ms * 1e3, 2),
+        "gemm_TFLOP_per_s": round(flops / (g_ms * 1e-3) / 1e12, 1),
+        "gemm_pct_fp4_peak": round(100 * flops / (g_ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 2),
+        "quantize_us": round(q_ms * 1e3, 2),
+        "quantize_GB_per_s": round(QUANT_BYTES_PER_ELEM * M * K / (q_ms * 1e-3) / 1e9, 1),
+        "reps": reps,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -242,6 +285,21 @@ def main():
 
     quant_ms = batch_ms(quantize, 100)
 
+    # the same pass with its inputs and outputs rotated over 8 buffer sets
+    # (514 MB, more than the 256 MB last-level cache), so that each launch
+    # reads X from HBM
+    cold_sets = [(x.clone(), torch.empty_like(qx), torch.empty_like(sx), torch.empty_like(qr), torch.empty_like(sr))
+                 for _ in range(8)]
+    cold_i = [0]
+
+    def quantize_cold():
+        xc, a, b, c, d = cold_sets[cold_i[0] % 8]
+        cold_i[0] += 1
+        rfq._lib.check(lib.rfq_residual_quantize(xc.data_ptr(), 0, M, K, xc.stride(0), a.data_ptr(), b.data_ptr(),
+                                                 c.data_ptr(), d.data_ptr(), sp))
+    cold_ms = batch_ms(quantize_cold, 96)
+    del cold_sets
+
     def rotated_quantize():
         rfq._lib.check(lib.rfq_rotate_residual_quantize(x.data_ptr(), 0, M, K, x.stride(0), qx.data_ptr(), sx.data_ptr(),
                                                         qr.data_ptr(), sr.data_ptr(), sp))
@@ -318,6 +376,8 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(gemm_ms * 1e3, 2),
             "median_launch_us": round(float(np.median(gemm_times)) * 1e3, 2),
+            "iqr_launch_us": [round(float(np.percentile(gemm_times, 25)) * 1e3, 2),
+                              round(float(np.percentile(gemm_times, 75)) * 1e3, 2)],
             "measured_mfma_ceiling": dict(ceiling, frac_of_ceiling=round(gemm_tflops / ceiling["TFLOP_per_s"], 4)),
         },
         "kernels": {
@@ -327,6 +387,12 @@ def main():
                 "pct_hbm_peak": round(100 * quant_gbs / HBM_PEAK_GBS, 2),
                 "algorithmic_bytes": QUANT_BYTES_PER_ELEM * M * K,
                 "note": "100 back-to-back launches; the 64 MB working set is partly served by the 256 MB last-level cache",
+            },
+            "quantize_residual_cold": {
+                "avg_launch_us": round(cold_ms * 1e3, 2),
+                "GB_per_s": round(QUANT_BYTES_PER_ELEM * M * K / (cold_ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * QUANT_BYTES_PER_ELEM * M * K / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "note": "96 launches rotating over 8 input/output buffer sets (514 MB): X comes from HBM",
             },
             "quantize_residual_rotated": {
                 "avg_launch_us": round(rot_ms * 1e3, 2),
@@ -373,9 +439,22 @@ def main():
             },
         },
     }
+    sweep = {}
+    if not args.no_sweep:
+        sweep[cfg.name] = layer_timings(rfq, torch, cfg, x, wq, sw, batch_ms, 50)
     del qx, qr, sx, sr, y, x
 
-    if not args.no_hbm_quantize:
+    if not args.no_sweep:
+        for name in ("tiny", "qwen3vl_attn_proj", "qwen3vl_ffn_up", "wan22_ffn"):
+            if name in sweep:
+                continue
+            c = workloads.CONFIGS[name]
+            xc = to_dev(workloads.x_bf16(c))
+            wqc, swc = rfq.quantize_mxfp4(to_dev(workloads.w_bf16(c)))
+            sweep[name] = layer_timings(rfq, torch, c, xc, wqc, swc, batch_ms, 50)
+            del xc, wqc, swc
+
+    if not args.no_hbm_quantize or not args.no_sweep:
         # the quantize pass on the long-sequence layer, whose traffic (1.39 GB)
         # exceeds the 256 MB last-level cache, so the figure is HBM-bound
         c5 = workloads.CONFIGS["dit_ffn_down"]
@@ -394,6 +473,10 @@ def main():
                                                             s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
         q5r_ms = batch_ms(q5_rot, 20)
         gbs_rot = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5r_ms * 1e-3) / 1e9
+        if not args.no_sweep and "dit_ffn_down" not in sweep:
+            w5q, w5s = rfq.quantize_mxfp4(to_dev(workloads.w_bf16(c5)))
+            sweep["dit_ffn_down"] = layer_timings(rfq, torch, c5, x5, w5q, w5s, batch_ms, 10)
+            del w5q, w5s
         del x5, q5, s5
         # what a plain device-to-device copy reaches on this HBM (read + write)
         ca = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -418,6 +501,11 @@ def main():
             "bytes_moved": 2 * (1 << 30), "GB_per_s": round(copy_gbs, 1),
             "pct_hbm_peak": round(100 * copy_gbs / HBM_PEAK_GBS, 2),
         }
+
+    if sweep:
+        out["configs"] = dict(sweep, note="RFQ layer on each configuration: quantize + residual pass, K-doubled GEMM, "
+                                          "and the step (both back to back), averaged over back-to-back launches; "
+                                          "TFLOP/s count 4 M N K")
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
