@@ -27,6 +27,9 @@ Sources followed (cited by page title and section):
 * MXFP8 (``mxfp8.py``): E4M3 elements per OCP MX v1.0, for the W4A8 layer and
   for RFQ with an MXFP8 residual path (the pages study MXFP8 beside MXFP4,
   Abstract and §1); see that module.
+* The straight-through backward pass (``backward.py``): the pages present
+  RFQ as training-aware but do not write the backward out; see that module
+  for the reading taken.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against facts
 that do not come from this code (worked examples, closed forms, brute force,
@@ -55,6 +58,7 @@ from .quantize import (
 )
 from .gemm import gemm_w4a4, linear
 from .rotate import hadamard32_f32, linear_rotated, rotate_quantize_weight, rotate_residual_quantize
+from .backward import backward_dw, backward_dx, linear_backward
 from .mxfp8 import (
     E4M3_MAGNITUDES,
     E4M3_MAX,
@@ -81,4 +85,5 @@ __all__ = [
     "E4M3_MAGNITUDES", "E4M3_MAX", "e4m3_value", "scale_exponent_e4m3", "encode_e4m3",
     "quantize_mxfp8", "dequantize_mxfp8", "residual_quantize_fp8",
     "gemm_w4a8", "gemm_w4a4_fp8_residual", "linear_w4a8", "linear_fp8_residual",
+    "backward_dx", "backward_dw", "linear_backward",
 ]
