@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RFQ_ABI_VERSION 3
+#define RFQ_ABI_VERSION 4
 
 typedef enum rfq_status {
   RFQ_OK = 0,
@@ -204,6 +204,48 @@ rfq_status_t rfq_gemm_w4a4_mxfp8_residual(const uint8_t* qx_codes, const uint8_t
                                           const uint8_t* w_codes, const uint8_t* w_scales,
                                           int64_t M, int64_t N, int64_t K,
                                           void* y, int y_dtype, int64_t ldy, rfq_stream_t stream);
+
+/*
+ * Straight-through backward pass. The pages ("Activation Outliers Matter",
+ * §1) present RFQ as training-aware error modelling for low-bit training
+ * but do not write the backward pass out. With Q passing gradients through
+ * unchanged, the gradients of the forward product Y = Xh Wd^T
+ * (Xh = deq Q(X) + deq Q(R), Wd = deq Q(W)) are
+ *   dX = dY Wd                                      (contraction over N)
+ *   dW = dY^T Xh = dY^T deq Q(X) + dY^T deq Q(R)     (contraction over M)
+ * (the residual adds no gradient path to X: dR/dX = I - I = 0). Both are
+ * computed from the decoded operands, exactly, with fp32 accumulation (bf16
+ * matrix instructions; every product is exact in fp32).
+ *
+ * rfq_backward_dx - dX [M, K] from dY [M, N] (bf16, dense: lddy == N, N a
+ *   positive multiple of 8 and at most 2^22) and the weight's MXFP4 codes and
+ *   scales (as rfq_quantize_mxfp4 wrote them). dx: fp32 or bf16, stride
+ *   lddx >= K. workspace: at least rfq_backward_dx_workspace_size(N, K)
+ *   bytes, 256-byte aligned, device; on return it holds deq(Wq)^T [K, N]
+ *   bf16. M == 0 is a no-op.
+ * rfq_backward_dw - dW [N, K] from dY [M, N] (bf16, stride lddy >= N; M
+ *   positive and at most 2^22) and the forward's Q(X) and Q(R) codes and
+ *   scales (as rfq_residual_quantize wrote them). dw: fp32 or bf16, stride
+ *   lddw >= K. workspace: at least rfq_backward_dw_workspace_size(M, N, K)
+ *   bytes, 256-byte aligned, device; on return it holds dY^T [N, Mp],
+ *   deq Q(X)^T [K, Mp] and deq Q(R)^T [K, Mp] bf16 (Mp = M rounded up to a
+ *   multiple of 8, columns past M zero), each region rounded up to 256
+ *   bytes. N == 0 is a no-op.
+ * Decoded values must lie within bf16's range, which holds for scale codes
+ * up to 252 (every quantization of bf16 data). Errors as for the other
+ * entry points.
+ */
+size_t rfq_backward_dx_workspace_size(int64_t N, int64_t K);
+size_t rfq_backward_dw_workspace_size(int64_t M, int64_t N, int64_t K);
+rfq_status_t rfq_backward_dx(const void* dy, int dy_dtype, int64_t M, int64_t N, int64_t lddy,
+                             const uint8_t* w_codes, const uint8_t* w_scales, int64_t K,
+                             void* dx, int dx_dtype, int64_t lddx,
+                             void* workspace, size_t workspace_bytes, rfq_stream_t stream);
+rfq_status_t rfq_backward_dw(const void* dy, int dy_dtype, int64_t M, int64_t N, int64_t lddy,
+                             const uint8_t* qx_codes, const uint8_t* qx_scales,
+                             const uint8_t* qr_codes, const uint8_t* qr_scales, int64_t K,
+                             void* dw, int dw_dtype, int64_t lddw,
+                             void* workspace, size_t workspace_bytes, rfq_stream_t stream);
 
 /* Bytes of workspace rfq_linear needs for an [M, K] activation: Q(X) and
  * Q(R) codes and scales, each region rounded up to 256 bytes. Host only;

@@ -30,6 +30,8 @@ __all__ = [
     "residual_quantize_mxfp8",
     "gemm_w4a8",
     "gemm_w4a4_mxfp8_residual",
+    "backward_dx",
+    "backward_dw",
     "linear",
     "linear_workspace_size",
     "library",
@@ -161,6 +163,42 @@ def gemm_w4a4_mxfp8_residual(qx, sx, qr8, sr, wq, sw, out_dtype=torch.bfloat16, 
     check(load().rfq_gemm_w4a4_mxfp8_residual(_ptr(qx), _ptr(sx), _ptr(qr8), _ptr(sr), _ptr(wq), _ptr(sw), M, N, K,
                                               _ptr(y), _y_dtype(y.dtype), y.stride(0), _stream()))
     return y
+
+
+def _dy_args(dy):
+    if dy.dtype != torch.bfloat16 or dy.dim() != 2 or not dy.is_cuda or dy.stride(1) != 1:
+        raise ValueError("dy must be a 2-D bfloat16 CUDA tensor with unit stride along N")
+    return dy.shape[0], dy.shape[1], dy.stride(0)
+
+
+def backward_dx(dy, wq, sw, out_dtype=torch.float32, out=None, workspace=None):
+    """Straight-through dX = dY deq(Wq) for bf16 dY [M, N] (dense) and the
+    weight's MXFP4 codes/scales; returns dX [M, K]."""
+    M, N, lddy = _dy_args(dy)
+    _codes_ok(wq, sw)
+    K = wq.shape[1] * 2
+    dx = _out(out, M, K, out_dtype, dy.device)
+    need = int(load().rfq_backward_dx_workspace_size(N, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dy.device)
+    check(load().rfq_backward_dx(_ptr(dy), DTYPE_BF16, M, N, lddy, _ptr(wq), _ptr(sw), K, _ptr(dx), _y_dtype(dx.dtype),
+                                 dx.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    return dx
+
+
+def backward_dw(dy, qx, sx, qr, sr, out_dtype=torch.float32, out=None, workspace=None):
+    """Straight-through dW = dY^T (deq Q(X) + deq Q(R)) for bf16 dY [M, N] and
+    the forward's RFQ encoding of X; returns dW [N, K]."""
+    M, N, lddy = _dy_args(dy)
+    _codes_ok(qx, sx, qr, sr)
+    K = qx.shape[1] * 2
+    dw = _out(out, N, K, out_dtype, dy.device)
+    need = int(load().rfq_backward_dw_workspace_size(M, N, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dy.device)
+    check(load().rfq_backward_dw(_ptr(dy), DTYPE_BF16, M, N, lddy, _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), K, _ptr(dw),
+                                 _y_dtype(dw.dtype), dw.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    return dw
 
 
 def linear_workspace_size(M, K):

@@ -40,6 +40,10 @@ SIGNATURES = {
     "rfq_residual_quantize_mxfp8": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "rfq_gemm_w4a8": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _i64, _p]),
     "rfq_gemm_w4a4_mxfp8_residual": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _i64, _p]),
+    "rfq_backward_dx_workspace_size": (_sz, [_i64, _i64]),
+    "rfq_backward_dw_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "rfq_backward_dx": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _i64, _p, _i, _i64, _p, _sz, _p]),
+    "rfq_backward_dw": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _i64, _p, _i, _i64, _p, _sz, _p]),
 }
 
 _LIB = None

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librfq.so")
-SOURCES = ["quantize.hip", "gemm.hip", "probe.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "backward.hip", "probe.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -242,6 +242,90 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                                    s));
 }
 
+size_t rfq_backward_dx_workspace_size(int64_t N, int64_t K) {
+  if (N <= 0 || N % 8 != 0 || N > kMaxK || K <= 0 || K % 32 != 0 || K > kMaxK) return 0;
+  return round256((size_t)K * (size_t)N * 2);
+}
+
+size_t rfq_backward_dw_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > kMaxK || N <= 0 || N > kMaxRows || K <= 0 || K % 32 != 0 || K > kMaxK) return 0;
+  const size_t mp = (size_t)((M + 7) / 8 * 8);
+  return round256((size_t)N * mp * 2) + 2 * round256((size_t)K * mp * 2);
+}
+
+rfq_status_t rfq_backward_dx(const void* dy, int dy_dtype, int64_t M, int64_t N, int64_t lddy,
+                             const uint8_t* w_codes, const uint8_t* w_scales, int64_t K,
+                             void* dx, int dx_dtype, int64_t lddx,
+                             void* workspace, size_t workspace_bytes, rfq_stream_t stream) {
+  if (M < 0 || M > kMaxRows) return fail(RFQ_ERR_INVALID_SHAPE, "M = %lld out of range [0, 2^31)", (long long)M);
+  if (N <= 0 || N % 8 != 0 || N > kMaxK)
+    return fail(RFQ_ERR_INVALID_SHAPE, "N = %lld must be positive, a multiple of 8 and at most 2^22", (long long)N);
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_rows_k(N, K, "N"));
+  if (dy_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "dy_dtype %d: must be RFQ_DTYPE_BF16", dy_dtype);
+  if (dx_dtype != RFQ_DTYPE_FP32 && dx_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "dx_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", dx_dtype);
+  if (lddy != N) return fail(RFQ_ERR_INVALID_STRIDE, "lddy = %lld: dY must be dense (lddy == N)", (long long)lddy);
+  if (M == 0) return ok();
+  if (dy == nullptr) return fail(RFQ_ERR_NULL_POINTER, "dy is NULL");
+  if (!aligned(dy, 16)) return fail(RFQ_ERR_MISALIGNED, "dy must be 16-byte aligned");
+  RFQ_TRY(check_codes(w_codes, w_scales, "W"));
+  RFQ_TRY(check_y(dx, dx_dtype, K, lddx));
+  if (workspace == nullptr) return fail(RFQ_ERR_NULL_POINTER, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(RFQ_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  const size_t need = rfq_backward_dx_workspace_size(N, K);
+  if (workspace_bytes < need)
+    return fail(RFQ_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes = %zu, need %zu", workspace_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* wdt = static_cast<uint16_t*>(workspace);                      // deq(Wq)^T [K, N] bf16
+  hipError_t e = rfq::launch_decode_transpose(w_codes, w_scales, N, K, wdt, N, s);
+  if (e != hipSuccess) return launched(e);
+  return launched(rfq::launch_gemm(16, 0, static_cast<const uint8_t*>(dy), nullptr, nullptr, nullptr,
+                                   reinterpret_cast<const uint8_t*>(wdt), nullptr, M, K, 4 * N, dx,
+                                   dx_dtype == RFQ_DTYPE_BF16, lddx, s));
+}
+
+rfq_status_t rfq_backward_dw(const void* dy, int dy_dtype, int64_t M, int64_t N, int64_t lddy,
+                             const uint8_t* qx_codes, const uint8_t* qx_scales,
+                             const uint8_t* qr_codes, const uint8_t* qr_scales, int64_t K,
+                             void* dw, int dw_dtype, int64_t lddw,
+                             void* workspace, size_t workspace_bytes, rfq_stream_t stream) {
+  if (M <= 0 || M > kMaxK)
+    return fail(RFQ_ERR_INVALID_SHAPE, "M = %lld must be positive and at most 2^22", (long long)M);
+  if (N < 0 || N > kMaxRows) return fail(RFQ_ERR_INVALID_SHAPE, "N = %lld out of range [0, 2^31)", (long long)N);
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_rows_k(N, K, "N"));
+  if (dy_dtype != RFQ_DTYPE_BF16) return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "dy_dtype %d: must be RFQ_DTYPE_BF16", dy_dtype);
+  if (dw_dtype != RFQ_DTYPE_FP32 && dw_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "dw_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", dw_dtype);
+  if (lddy < N) return fail(RFQ_ERR_INVALID_STRIDE, "lddy = %lld must be >= N = %lld", (long long)lddy, (long long)N);
+  if (N == 0) return ok();
+  if (dy == nullptr) return fail(RFQ_ERR_NULL_POINTER, "dy is NULL");
+  if (!aligned(dy, 2)) return fail(RFQ_ERR_MISALIGNED, "dy must be 2-byte aligned");
+  RFQ_TRY(check_codes(qx_codes, qx_scales, "Q(X)"));
+  RFQ_TRY(check_codes(qr_codes, qr_scales, "Q(R)"));
+  RFQ_TRY(check_y(dw, dw_dtype, K, lddw));
+  if (workspace == nullptr) return fail(RFQ_ERR_NULL_POINTER, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(RFQ_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  const size_t need = rfq_backward_dw_workspace_size(M, N, K);
+  if (workspace_bytes < need)
+    return fail(RFQ_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes = %zu, need %zu", workspace_bytes, need);
+  const int64_t mp = (M + 7) / 8 * 8;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* dyt = reinterpret_cast<uint16_t*>(ws);                                          // dY^T [N, Mp]
+  uint16_t* xqt = reinterpret_cast<uint16_t*>(ws + round256((size_t)N * mp * 2));            // deq Q(X)^T [K, Mp]
+  uint16_t* xrt = reinterpret_cast<uint16_t*>(ws + round256((size_t)N * mp * 2) + round256((size_t)K * mp * 2));
+  hipError_t e = rfq::launch_transpose_bf16(static_cast<const uint16_t*>(dy), M, N, lddy, dyt, mp, s);
+  if (e == hipSuccess) e = rfq::launch_decode_transpose(qx_codes, qx_scales, M, K, xqt, mp, s);
+  if (e == hipSuccess) e = rfq::launch_decode_transpose(qr_codes, qr_scales, M, K, xrt, mp, s);
+  if (e != hipSuccess) return launched(e);
+  // dW^T [K, N] = Xq^T-rows . dY^T-rows + Xr^T-rows . dY^T-rows over Mp, stored transposed as dW [N, K]
+  return launched(rfq::launch_gemm(16, 16, reinterpret_cast<const uint8_t*>(xqt), nullptr,
+                                   reinterpret_cast<const uint8_t*>(xrt), nullptr, reinterpret_cast<const uint8_t*>(dyt),
+                                   nullptr, K, N, 4 * mp, dw, dw_dtype == RFQ_DTYPE_BF16, lddw, s, true));
+}
+
 const char* rfq_status_string(rfq_status_t status) {
   switch (status) {
     case RFQ_OK: return "success";

@@ -62,6 +62,7 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBK = 128;                            // K elements per stage
@@ -87,21 +88,36 @@ constexpr int kGroupM = 4;                          // tile rows swept together 
 // 2 s + lhalf (the chunk an MFMA lane reads in step s), the 16-byte row
 // chunks 4 s + lhalf (first sub-tile) and 4 s + 2 + lhalf (second): row chunk
 // 4 (c / 2) + (c % 2), plus 2 for the second sub-tile.
-template <int kX, int kR>
+//
+// Format 16 is bfloat16 for every operand (the weight operand too), with no
+// scales: the straight-through backward's products of decoded values. A
+// stage row is then 64 bytes = 32 elements, two K-steps of the bf16
+// 32x32x16 MFMA, whose 16-byte fragments are read exactly like the E2M1
+// ones. kT: the result is stored transposed (element (r, c) of the tile to
+// y[c * ldy + r]).
+template <int kX, int kR, bool kT = false>
 struct Fmts {
   static constexpr int kXFmt = kX, kRFmt = kR;
   static constexpr bool kResid = kR != 0;
+  static constexpr bool kBf16 = kX == 16;
+  static constexpr bool kOutT = kT;
   static constexpr int kXSub = kX == 8 ? 2 : 1;
-  static constexpr int kRSub = kR == 8 ? 2 : (kR == 4 ? 1 : 0);
+  static constexpr int kRSub = kR == 8 ? 2 : (kR != 0 ? 1 : 0);
   static constexpr int kSubA = kXSub + kRSub;          // activation sub-tiles per stage
-  static constexpr int kScalesA = kResid ? 2 : 1;      // activation scale streams
+  static constexpr int kScalesA = kBf16 ? 0 : (kResid ? 2 : 1);   // activation scale streams
+  static constexpr int kScalesB = kBf16 ? 0 : 1;       // weight scale stream
   static constexpr int kTerms = kResid ? 2 : 1;        // MFMAs per output tile per step
-  static_assert((kX == 4 || kX == 8) && (kR == 0 || kR == 4 || kR == 8) && !(kX == 8 && kR != 0), "formats");
+  static_assert((kX == 4 && (kR == 0 || kR == 4 || kR == 8)) || (kX == 8 && kR == 0) ||
+                    (kX == 16 && (kR == 0 || kR == 16)),
+                "formats");
+  static_assert(!kT || kBf16, "transposed stores are for the bf16 products");
 };
 using FmtW4A4 = Fmts<4, 0>;
 using FmtRfq = Fmts<4, 4>;
 using FmtW4A8 = Fmts<8, 0>;
 using FmtRfq8 = Fmts<4, 8>;
+using FmtBf16 = Fmts<16, 0>;                // dX = dY Wd: bf16 x bf16
+using FmtBf16PairT = Fmts<16, 16, true>;    // dW^T = Xq dY^T + Xr dY^T, stored as dW
 
 // MFMA format code of an element format: E4M3 is 0, E2M1 is 4.
 template <int kFmt>
@@ -119,7 +135,7 @@ struct TileCfg {
   static constexpr int kTileBytesA = kBM * kRowBytes, kTileBytesB = kBN * kRowBytes;   // one sub-tile
   static constexpr int kStageBytes = F::kSubA * kTileBytesA + kTileBytesB;
   static constexpr int kScaleBytesA = kBM * kScaleRowBytes;
-  static constexpr int kScaleBytes = F::kScalesA * kScaleBytesA + kBN * kScaleRowBytes;
+  static constexpr int kScaleBytes = F::kScalesA * kScaleBytesA + F::kScalesB * kBN * kScaleRowBytes;
   static constexpr int kLdsBytes = kRing * kStageBytes + kScaleBytes;
   static constexpr int kLoadsA = kBM / 16 / kWaves;    // 16-row DMA instructions per wave per sub-tile of X / R
   static constexpr int kLoadsB = kBN / 16 / kWaves;    // for W
@@ -168,6 +184,9 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 2) & 3u; }
 // The kernel's parameter block, read again from the kernel-argument segment.
 // Code that runs once per tile uses it instead of values held since the
 // kernel started, so those do not occupy scalar registers through the loop.
+// It must be inlined into the kernel itself: in a called function the
+// segment pointer is not passed along (the compiler substitutes 0), which is
+// why every lambda of the kernel body is marked always_inline.
 typedef __attribute__((address_space(4))) const GemmParams* const_params_ptr;
 __device__ __forceinline__ GemmParams fresh_params() {
   const_params_ptr q = (const_params_ptr)__builtin_amdgcn_kernarg_segment_ptr();
@@ -248,6 +267,17 @@ template <int S, class F, int kTM, int kTN>
 __device__ __forceinline__ void mfma_step(f32x16_t (&acc)[kTM][kTN], const i32x4_t (&a)[F::kSubA][kTM],
                                           const i32x4_t (&b)[kTN], const uint32_t (&scx)[kTM],
                                           const uint32_t (&scr)[kTM], const uint32_t (&scw)[kTN]) {
+  if constexpr (F::kBf16) {
+#pragma unroll
+    for (int t = 0; t < F::kSubA; ++t)
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
+                                                              __builtin_bit_cast(bf16x8_t, a[t][i]), acc[i][j], 0, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kTM; ++i) {
     const i32x8_t ax = term_operand<F::kXFmt, 0, F::kSubA, kTM>(a, i);
@@ -329,7 +359,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // starts 32 bytes (two chunks) into the row, so the same offsets fetch it.
   const uint32_t kbytes = (uint32_t)p.K / 2, kblocks = (uint32_t)p.K / 32;
   __amdgpu_buffer_rsrc_t ra[kSubA], rw, rsx, rsr, rsw;
-  auto set_load_tile = [&](const GemmParams& q, int m0, int n0) {
+  auto set_load_tile = [&](const GemmParams& q, int m0, int n0) __attribute__((always_inline)) {
     const uint32_t rows_a = (uint32_t)min(kBM, q.M - m0), rows_b = (uint32_t)min(kBN, q.N - n0);
     const uint32_t xrow = F::kXFmt == 8 ? 2 * kbytes : kbytes, rrow = F::kRFmt == 8 ? 2 * kbytes : kbytes;
     ra[0] = make_rsrc(q.qx + (int64_t)m0 * xrow, rows_a * xrow);
@@ -339,9 +369,11 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       if constexpr (F::kRFmt == 8) ra[F::kXSub + 1] = make_rsrc(q.qr + (int64_t)m0 * rrow + 32, rows_a * rrow - 32);
     }
     rw = make_rsrc(q.w + (int64_t)n0 * kbytes, rows_b * kbytes);
-    rsx = make_rsrc(q.sx + (int64_t)m0 * kblocks, rows_a * kblocks);
-    rsr = make_rsrc(kResid ? q.sr + (int64_t)m0 * kblocks : q.sx, rows_a * kblocks);
-    rsw = make_rsrc(q.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
+    if constexpr (!F::kBf16) {
+      rsx = make_rsrc(q.sx + (int64_t)m0 * kblocks, rows_a * kblocks);
+      rsr = make_rsrc(kResid ? q.sr + (int64_t)m0 * kblocks : q.sx, rows_a * kblocks);
+      rsw = make_rsrc(q.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
+    }
   };
   set_load_tile(p, cm0, cn0);
   int load_tile = 0, load_base = 0;              // tile being fetched and its first stream stage
@@ -364,7 +396,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     ldb_voff[n] = row * kbytes + 16 * ldb_chunk[n];
   }
   // byte offset of a lane's chunk in stage 0 of an activation term of format kFmt
-  auto lda_voff = [&](auto fmt_c, int n) -> uint32_t {
+  auto lda_voff = [&](auto fmt_c, int n) __attribute__((always_inline)) -> uint32_t {
     constexpr int fmt = decltype(fmt_c)::value;
     return fmt == 8 ? lda_row[n] * (2 * kbytes) + 64 * (lda_chunk[n] >> 1) + 16 * (lda_chunk[n] & 1)
                     : lda_row[n] * kbytes + 16 * lda_chunk[n];
@@ -378,15 +410,15 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // slots repeat pieces (identical bytes to the same place), so every wave
   // issues as many loads
   constexpr int kPiecesA = kBM / 64, kPiecesB = kBN / 64;
-  constexpr int kPieces = F::kScalesA * kPiecesA + kPiecesB;
-  constexpr int kScaleLoadsPerWave = (kPieces + kWaves - 1) / kWaves;
+  constexpr int kPieces = F::kScalesA * kPiecesA + F::kScalesB * kPiecesB;
+  constexpr int kScaleLoadsPerWave = (kPieces + kWaves - 1) / kWaves;   // 0 without scales
 
   // Stream stage st (stage st - load_base of the tile being fetched). A
   // stage past the end of the stream is still issued, at an out-of-range
   // offset: it writes zeros into a slot nothing reads again, and keeps the
   // number of loads per stage constant. The loads go out in two parts.
   constexpr int kPart0 = (kDmaPerStage + 1) / 2;
-  auto issue_stage = [&](int st, auto part_c) {
+  auto issue_stage = [&](int st, auto part_c) __attribute__((always_inline)) {
     constexpr int part = decltype(part_c)::value;   // 0: first kPart0 loads, 1: the rest, 2: all
     uint8_t* buf = ring + (st % kRing) * kStageBytes;
     const int kst = st - load_base;
@@ -421,7 +453,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
 
   // Scale group g of the tile being fetched: 16 bytes (blocks 16 g .. 16 g +
   // 15) of every row of X, R and W, as 64-row pieces.
-  auto issue_scale_piece = [&](__amdgpu_buffer_rsrc_t r, int g, int op, int q) {
+  auto issue_scale_piece = [&](__amdgpu_buffer_rsrc_t r, int g, int op, int q) __attribute__((always_inline)) {
     // (the lane index is re-read here so that the row offset is recomputed
     // once per group instead of occupying a register through the loop)
     uint32_t lane_now = lane;
@@ -448,11 +480,12 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       *reinterpret_cast<i32x4_t*>(dst + lane * kScaleRowBytes) = i32x4_t{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
     }
   };
-  auto issue_scales = [&](int stream_g) {
+  auto issue_scales = [&](int stream_g) __attribute__((always_inline)) {
+    if constexpr (kPieces == 0) return;
     const int g = stream_g - load_base / kScaleGroup;   // past the stream end: g >= ngroups
 #pragma unroll
     for (int t = 0; t < kScaleLoadsPerWave; ++t) {
-      const int j = (kScaleLoadsPerWave * (int)wave + t) % kPieces;   // wave-uniform
+      const int j = (kScaleLoadsPerWave * (int)wave + t) % (kPieces > 0 ? kPieces : 1);   // wave-uniform
       if (j < kPiecesA)
         issue_scale_piece(rsx, g, 0, j);
       else if (kResid && j < 2 * kPiecesA)
@@ -488,7 +521,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   };
   // this lane's scale words for two stages (a pair of the group's four)
   i32x2_t gx[kTM], gr[kTM], gw[kTN];
-  auto read_scale_pair = [&](int pair) {
+  auto read_scale_pair = [&](int pair) __attribute__((always_inline)) {
+    if constexpr (F::kBf16) return;
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const uint8_t* s0 = sbuf + (a_row0 + 32 * i + lrow) * kScaleRowBytes + 8 * pair;
@@ -502,7 +536,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   };
 
   f32x16_t acc[kTM][kTN];
-  auto zero_acc = [&]() {
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -530,13 +564,14 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
 
   // One stage; P = st % 4 is a compile-time constant so that every wait count
   // and scale-word index below is one.
-  auto stage = [&](auto pc, int st) {
+  auto stage = [&](auto pc, int st) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
     __builtin_amdgcn_sched_barrier(0);   // keep each stage's schedule to itself
     // scale words of this stage: byte 2 s of (word >> 8 lhalf) is block 4 st + 2 s + lhalf
     // (the empty asm pins each extraction in its own stage, so the compiler
     // does not compute all four stages' words up front and hold them)
     uint32_t cx[kTM], cr[kTM], cw[kTN];
+    if constexpr (!F::kBf16) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       cx[i] = (uint32_t)gx[i][P % 2];
@@ -555,6 +590,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       cw[j] = (uint32_t)gw[j][P % 2];
       asm volatile("" : "+v"(cw[j]));
       cw[j] >>= 8 * lhalf;
+    }
     }
 
     // first MFMA step; meanwhile read the second step's fragments and issue
@@ -610,10 +646,38 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // Y and, in accumulator group q / 4, the four consecutive columns
   // 8 (q / 4) + 4 lhalf + (0..3), stored together (8 bytes of bf16 or 16 of
   // fp32) when the host found Y's base and row stride aligned for it.
-  auto store_tile = [&](int em0, int en0) {
+  auto store_tile = [&](int em0, int en0) __attribute__((always_inline)) {
     const GemmParams q = fresh_params();
     const int row_base = em0 + (int)a_row0 + (int)lrow;
     const int col_base = en0 + (int)b_row0 + 4 * (int)lhalf;
+    if constexpr (F::kOutT) {
+      // element (row, col) to y[col * ldy + row]: for one (i, j, g, e) the 32
+      // lanes of a half write 32 consecutive rows of one output row
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int row = row_base + 32 * i;
+        if (row >= q.M) continue;
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int col = col_base + 32 * j + 8 * g + e;
+              if (col >= q.N) continue;
+              const float v = acc[i][j][4 * g + e];
+              const int64_t at = (int64_t)col * q.ldy + row;
+              if (kOutBf16) {
+                const uint32_t u = __builtin_bit_cast(uint32_t, v);
+                reinterpret_cast<uint16_t*>(q.y)[at] =
+                    (uint16_t)(((v != v) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+              } else {
+                reinterpret_cast<float*>(q.y)[at] = v;
+              }
+            }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const int row = row_base + 32 * i;
@@ -659,7 +723,11 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // store is scheduled on its own (sched_barrier), so that only one group of
   // converted values is live at a time: this runs inside the K loop, beside
   // the next tile's fragments.
-  auto store_full_tile = [&](int em0, int en0) {
+  auto store_full_tile = [&](int em0, int en0) __attribute__((always_inline)) {
+    if constexpr (F::kOutT) {
+      store_tile(em0, en0);
+      return;
+    }
     const GemmParams q = fresh_params();
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -777,17 +845,28 @@ int cu_count() {
 
 hipError_t launch_gemm(int x_fmt, int r_fmt, const uint8_t* qx, const uint8_t* sx, const uint8_t* qr,
                        const uint8_t* sr, const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N, int64_t K,
-                       void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
+                       void* y, bool y_bf16, int64_t ldy, hipStream_t stream, bool y_trans) {
   GemmParams p;
   p.qx = qx; p.sx = sx; p.qr = qr; p.sr = sr; p.w = w; p.sw = sw;
   p.y = y; p.ldy = ldy;
-  // four consecutive outputs go out as one 8-byte (bf16) or 16-byte (fp32) store
+  // four consecutive outputs go out as one 8-byte (bf16) or 16-byte (fp32)
+  // store (transposed results go element by element, any alignment)
   const uintptr_t vec_bytes = y_bf16 ? 8 : 16;
-  p.vec_out = ((uintptr_t)y % vec_bytes == 0 && ldy % 4 == 0) ? 1 : 0;
+  p.vec_out = (y_trans || ((uintptr_t)y % vec_bytes == 0 && ldy % 4 == 0)) ? 1 : 0;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
   const bool fast = (K % (kBK * kScaleGroup)) == 0;
   const int cus = cu_count();
   if (qr == nullptr) r_fmt = 0;
+  if (x_fmt == 16) {
+    // bf16 operands: K counts E2M1-sized elements, 4 per bf16 element, so
+    // that bytes per row, stages and 16-byte chunks follow the same rules
+    if (y_trans != (r_fmt == 16)) return hipErrorInvalidValue;
+    if (r_fmt == 16)
+      return y_bf16 ? launch_variant<FmtBf16PairT, true>(p, fast, cus, stream)
+                    : launch_variant<FmtBf16PairT, false>(p, fast, cus, stream);
+    return y_bf16 ? launch_variant<FmtBf16, true>(p, fast, cus, stream) : launch_variant<FmtBf16, false>(p, fast, cus, stream);
+  }
+  if (y_trans) return hipErrorInvalidValue;
   switch (x_fmt * 10 + r_fmt) {
     case 40: return y_bf16 ? launch_variant<FmtW4A4, true>(p, fast, cus, stream) : launch_variant<FmtW4A4, false>(p, fast, cus, stream);
     case 44: return y_bf16 ? launch_variant<FmtRfq, true>(p, fast, cus, stream) : launch_variant<FmtRfq, false>(p, fast, cus, stream);

@@ -19,9 +19,23 @@ hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int x_fmt, int
 // qr != nullptr), with QX in format x_fmt and QR in r_fmt (4: MXFP4, 8:
 // MXFP8 E4M3). Supported: (4, -), (4, 4), (4, 8), (8, -); others return
 // hipErrorInvalidValue.
+//
+// x_fmt 16: bfloat16 operands throughout, no scales (r_fmt 0 or 16, the second
+// pair sharing w); K then counts four per bf16 element (bytes per row = K/2),
+// and y_trans (required with r_fmt 16, refused otherwise) stores the result
+// transposed: element (m, n) to y[n * ldy + m].
 hipError_t launch_gemm(int x_fmt, int r_fmt, const uint8_t* qx, const uint8_t* sx, const uint8_t* qr,
                        const uint8_t* sr, const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N, int64_t K,
-                       void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
+                       void* y, bool y_bf16, int64_t ldy, hipStream_t stream, bool y_trans = false);
+
+// Backward-pass operand staging (csrc/backward.hip): MXFP4 codes [rows,
+// cols/2] + scales to bf16 [cols, ld_out] transposed, and a bf16 transpose
+// [rows, cols] (stride ld_in) to [cols, ld_out]; columns past `rows` are
+// zero-filled. ld_out a multiple of 8, pointers 16-byte aligned.
+hipError_t launch_decode_transpose(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                                   uint16_t* out, int64_t ld_out, hipStream_t stream);
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld_in, uint16_t* out,
+                                 int64_t ld_out, hipStream_t stream);
 
 // Measurement probe: the scaled MFMA loop on caller-supplied operands (first
 // operand E2M1, second E2M1 or, b_fmt 8, E4M3).

@@ -91,3 +91,24 @@ def check_y(y_gpu, y_ref, s_ref, out_dtype, what="", extra=None):
     assert bad.size == 0, f"{what}: {len(bad)} outputs out of tolerance, first {bad[:3].tolist()}, " \
                           f"max |dY|/S = {worst:.3e}"
     return worst
+
+
+def check_grad(g_gpu, g_ref, s_ref, contraction, out_dtype, what=""):
+    """Per-output check of a straight-through gradient computed with bf16
+    matrix instructions: products of bf16 dY and decoded MXFP4 values are
+    exact in fp32, each instruction adds 16 of them, and its result goes into
+    the fp32 accumulator with one rounding (measured on gfx950: the sum
+    comes back within an fp32 ulp of exact, sometimes truncated), so
+    |dG| <= (ceil(P / 16) + 1) 2^-23 S over a contraction of length P; bf16
+    output adds the RNE half-ulp."""
+    g_gpu = np.asarray(g_gpu, dtype=np.float64)
+    steps = -(-int(contraction) // 16) + 1
+    tol = steps * 2.0 ** -23 * s_ref + 2.0 ** -126
+    if out_dtype == torch.bfloat16:
+        tol = tol * (1 + BF16_HALF_ULP) + BF16_HALF_ULP * np.abs(g_ref) + 2.0 ** -133
+    err = np.abs(g_gpu - g_ref)
+    bad = np.argwhere(~(err <= tol))
+    worst = float(np.max(err / np.maximum(s_ref, 1e-300)))
+    assert bad.size == 0, f"{what}: {len(bad)} outputs out of tolerance, first {bad[:3].tolist()}, " \
+                          f"max |dG|/S = {worst:.3e}"
+    return worst

@@ -36,11 +36,11 @@ def declared_functions():
 
 def test_header_declarations_are_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
-    assert lib.rfq_abi_version() == 3
+    assert lib.rfq_abi_version() == 4
 
 
 def status_name(st):
@@ -176,3 +176,35 @@ def test_mxfp8_entry_points_validation(lib):
     assert status_name(gr8(FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 0, 8, None)) == "RFQ_ERR_MISALIGNED"
     assert status_name(gr8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 64, FAKE + 1, 1, 8, None)) == "RFQ_ERR_MISALIGNED"
     assert status_name(gr8(None, None, None, None, None, None, 8, 0, 64, None, 0, 8, None)) == "RFQ_OK"
+
+
+def test_backward_validation(lib):
+    dx, dw = lib.rfq_backward_dx, lib.rfq_backward_dw
+    wsx = lib.rfq_backward_dx_workspace_size(64, 96)
+    assert wsx == (96 * 64 * 2 + 255) // 256 * 256
+    assert lib.rfq_backward_dx_workspace_size(60, 96) == 0          # N not a multiple of 8
+    mp = 104
+    assert lib.rfq_backward_dw_workspace_size(100, 40, 96) == ((40 * mp * 2 + 255) // 256 * 256
+                                                                 + 2 * ((96 * mp * 2 + 255) // 256 * 256))
+    def bx(dy=FAKE, dt=0, M=8, N=64, ld=64, w=FAKE, sw=FAKE, K=96, out=FAKE, od=1, ldo=96, ws=FAKE, n=wsx):
+        return status_name(dx(dy, dt, M, N, ld, w, sw, K, out, od, ldo, ws, n, None))
+    assert bx(N=60, ld=60) == "RFQ_ERR_INVALID_SHAPE"
+    assert bx(K=80) == "RFQ_ERR_INVALID_SHAPE"
+    assert bx(dt=1) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert bx(ld=72) == "RFQ_ERR_INVALID_STRIDE"
+    assert bx(dy=None) == "RFQ_ERR_NULL_POINTER"
+    assert bx(dy=FAKE + 2) == "RFQ_ERR_MISALIGNED"
+    assert bx(n=wsx - 1) == "RFQ_ERR_WORKSPACE_TOO_SMALL"
+    assert bx(ws=FAKE + 16) == "RFQ_ERR_MISALIGNED"
+    assert bx(ldo=90) == "RFQ_ERR_INVALID_STRIDE"
+    assert bx(M=0, dy=None, w=None, out=None, ws=None) == "RFQ_OK"
+    wsw = lib.rfq_backward_dw_workspace_size(8, 40, 96)
+    def bw(dy=FAKE, M=8, N=40, ld=40, qx=FAKE, qr=FAKE, K=96, out=FAKE, od=0, ldo=96, ws=FAKE, n=wsw):
+        return status_name(dw(dy, 0, M, N, ld, qx, FAKE, qr, FAKE, K, out, od, ldo, ws, n, None))
+    assert bw(M=0) == "RFQ_ERR_INVALID_SHAPE"
+    assert bw(ld=30) == "RFQ_ERR_INVALID_STRIDE"
+    assert bw(qr=None) == "RFQ_ERR_NULL_POINTER"
+    assert bw(qx=FAKE + 4) == "RFQ_ERR_MISALIGNED"
+    assert bw(n=wsw - 1) == "RFQ_ERR_WORKSPACE_TOO_SMALL"
+    assert bw(od=3) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert bw(N=0, dy=None, qx=None, qr=None, out=None, ws=None) == "RFQ_OK"
