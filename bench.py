@@ -31,6 +31,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 MFMA, TFLOP/s
 FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 / MXFP8 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense BF16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "RFQ W4A4 linear effective TFLOP/s (% MXFP4 peak); quantize GB/s (% HBM)"
 QUANT_BYTES_PER_ELEM = 2 + 2 * (0.5 + 1.0 / 32)      # bf16 in, Q(X) and Q(R) codes + scales out
@@ -344,6 +345,25 @@ def main():
     rfq8_tf = 4.0 * M * N * K / (rfq8_ms * 1e-3) / 1e12
     del qx8, qr8
 
+    # straight-through backward pass of the same layer: dX = dY deq(Wq) and
+    # dW = dY^T (deq Q(X) + deq Q(R)), each one entry-point call (operand
+    # staging + bf16 GEMM); dY is a seeded N(0, 1) bf16 tensor
+    quantize()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    dy = torch.randn((M, N), generator=gen, device=dev).to(torch.bfloat16)
+    ws_dx = torch.empty(lib.rfq_backward_dx_workspace_size(N, K), dtype=torch.uint8, device=dev)
+    ws_dw = torch.empty(lib.rfq_backward_dw_workspace_size(M, N, K), dtype=torch.uint8, device=dev)
+    g_dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    g_dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    bdx_ms = batch_ms(lambda: rfq._lib.check(lib.rfq_backward_dx(
+        dy.data_ptr(), 0, M, N, N, wq.data_ptr(), sw.data_ptr(), K, g_dx.data_ptr(), rfq._lib.DTYPE_BF16, K,
+        ws_dx.data_ptr(), ws_dx.numel(), sp)), 20)
+    bdw_ms = batch_ms(lambda: rfq._lib.check(lib.rfq_backward_dw(
+        dy.data_ptr(), 0, M, N, N, qx.data_ptr(), sx.data_ptr(), qr.data_ptr(), sr.data_ptr(), K, g_dw.data_ptr(),
+        rfq._lib.DTYPE_BF16, K, ws_dw.data_ptr(), ws_dw.numel(), sp)), 20)
+    del dy, ws_dx, ws_dw, g_dx, g_dw
+
     kernel_hash = source_hash("gemm.hip")
     traffic = counter_traffic(args.workload, kernel_hash)
     out = {
@@ -431,6 +451,19 @@ def main():
                 "over_rfq_time": round(rfq8_ms / gemm_ms, 3),
                 "note": "128 x 256 tiles; per output tile the E2M1 x E4M3 residual MFMAs take twice the cycles of the "
                         "E2M1 ones, so the instruction-time floor is 1.5x the RFQ GEMM's",
+            },
+            "backward_dx": {
+                "avg_call_us": round(bdx_ms * 1e3, 2),
+                "TFLOP_per_s_2MNK": round(2.0 * M * N * K / (bdx_ms * 1e-3) / 1e12, 1),
+                "pct_bf16_peak": round(100 * 2.0 * M * N * K / (bdx_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+                "what": "dX = dY deq(Wq) (rfq_backward_dx: decode-transpose of Wq, then the bf16 GEMM), bf16 dX",
+            },
+            "backward_dw": {
+                "avg_call_us": round(bdw_ms * 1e3, 2),
+                "TFLOP_per_s_4MNK": round(4.0 * M * N * K / (bdw_ms * 1e-3) / 1e12, 1),
+                "pct_bf16_peak": round(100 * 4.0 * M * N * K / (bdw_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+                "what": "dW = dY^T (deq Q(X) + deq Q(R)) (rfq_backward_dw: transposes of dY, Q(X), Q(R), then the "
+                        "K-doubled bf16 GEMM with transposed store), bf16 dW",
             },
             "gemm_plain_w4a4": {
                 "avg_launch_us": round(w4a4_ms * 1e3, 2),
