@@ -20,6 +20,9 @@
 // on the way back. The residual never leaves fp32 registers.
 //
 // Traffic per element: 2 B read, 2 x (0.5 + 1/32) B written = 3.0625 B.
+// X is read and the codes written with non-temporal accesses: each byte is
+// touched once, and streaming it past the caches measured 8% faster on a
+// layer larger than the last-level cache (75% of HBM peak against 69%).
 //
 // Variants of the same pass:
 //  * fp32 input (8 values = 32 bytes per lane);
@@ -145,9 +148,9 @@ __device__ __forceinline__ u32x2_t encode_part(const float* f, unsigned code) {
 template <int kFmt>
 __device__ __forceinline__ void store_part(uint8_t* q, uint32_t g, uint32_t part, u32x2_t c) {
   if constexpr (kFmt == 8)
-    *reinterpret_cast<u32x2_t*>(q + (uint64_t)g * 32 + part * 8) = c;
+    __builtin_nontemporal_store(c, reinterpret_cast<u32x2_t*>(q + (uint64_t)g * 32 + part * 8));
   else
-    *reinterpret_cast<unsigned*>(q + (uint64_t)g * 16 + part * 4) = c.x;
+    __builtin_nontemporal_store(c.x, reinterpret_cast<unsigned*>(q + (uint64_t)g * 16 + part * 4));
 }
 
 // r[2J], r[2J+1] = x[2J], x[2J+1] minus their decoded codes (byte J of
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     const u32x4_t* src = kF32In ? reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + elem)
                                 : reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + elem);
 #pragma unroll
-    for (int h = 0; h < kLoads; ++h) w[u][h] = (g < p.total_blocks) ? src[h] : u32x4_t{0, 0, 0, 0};
+    for (int h = 0; h < kLoads; ++h) w[u][h] = (g < p.total_blocks) ? __builtin_nontemporal_load(src + h) : u32x4_t{0, 0, 0, 0};
   }
 
 #pragma unroll
