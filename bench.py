@@ -120,6 +120,54 @@ def cpu_baseline(cfg):
     }
 
 
+def oracle_config_timings():
+    """The oracle on a bounded sample of every configuration: the residual
+    quantization of up to 1024 rows of X (one thread: GB/s of the pass's
+    algorithmic bytes), and the K-doubled float64 GEMM of those rows against
+    up to 2048 rows of W on all BLAS threads and, on 128 rows, on one thread.
+    The step time is extrapolated from the sample's rates (a small GEMM
+    sample runs BLAS less efficiently than the full layer would)."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threadpool_limits = None
+        blas_threads = os.cpu_count() or 1
+    out = {}
+    for name, c in workloads.CONFIGS.items():
+        q_rows, g_rows, n_cols = min(c.M, 1024), min(c.M, 1024), min(c.N, 2048)
+        x = oracle.bf16_bits_to_f64(workloads.x_bf16(c, 0, q_rows))
+        w = oracle.bf16_bits_to_f64(workloads.w_bf16(c)[:n_cols])
+        wq, sw = oracle.quantize_mxfp4(w)
+        t0 = time.perf_counter()
+        qx, sx, qr, sr = oracle.residual_quantize(x)
+        t_q = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_w4a4(qx[:g_rows], sx[:g_rows], qr[:g_rows], sr[:g_rows], wq, sw)
+        t_g = time.perf_counter() - t0
+        r1 = min(g_rows, 128)
+        t1 = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                oracle.gemm_w4a4(qx[:r1], sx[:r1], qr[:r1], sr[:r1], wq, sw)
+                t1 = time.perf_counter() - t0
+        gbs = QUANT_BYTES_PER_ELEM * q_rows * c.K / t_q / 1e9
+        tf = 4.0 * g_rows * n_cols * c.K / t_g / 1e12
+        t_step = QUANT_BYTES_PER_ELEM * c.M * c.K / (gbs * 1e9) + 4.0 * c.M * c.N * c.K / (tf * 1e12)
+        out[name] = {
+            "quantize_GB_per_s_1_thread": round(gbs, 4),
+            "gemm_TFLOP_per_s": round(tf, 5),
+            "gemm_TFLOP_per_s_1_thread": round(4.0 * r1 * n_cols * c.K / t1 / 1e12, 5) if t1 else None,
+            "step_s_extrapolated": round(t_step, 2),
+            "sample": f"quantize {q_rows} rows; GEMM {g_rows} x {n_cols} outputs ({blas_threads} threads), "
+                      f"{r1} x {n_cols} (1 thread)",
+        }
+    return out
+
+
 def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=None):
     """The power-limited ceiling of the GEMM's instruction on this workload's
     own operand bytes: rfq_probe_mfma_ceiling runs only scaled FP4 MFMAs (no
@@ -550,6 +598,8 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
+        if not args.no_sweep:
+            out["cpu_baseline"]["per_config"] = oracle_config_timings()
     print(json.dumps(out), flush=True)
     return 0
 
