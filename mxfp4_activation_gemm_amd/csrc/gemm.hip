@@ -22,8 +22,10 @@
 // outputs = 2 x 4 MFMA tiles (128 fp32 accumulators per lane). K advances
 // 128 elements (64 bytes of codes per row) per stage, as two MFMA steps of
 // 64. When the tile count leaves a last partial round on the CUs, that
-// round's tiles are split into 128 x 128 quadrants run by 4-wave workgroups,
-// two per CU, in a second launch.
+// round's tiles are split, in a second launch, into upper and lower halves
+// (128 x 256 on 8 waves of 32 x 128, one workgroup per CU) or, for the
+// formats whose main tile is already 128 rows, into quadrants (4 waves,
+// two workgroups per CU).
 //
 // Data movement:
 //  * Code tiles (QX, QR, W; 256 rows x 64 B each per stage) go global ->
@@ -144,19 +146,24 @@ struct TileCfg {
 };
 // Main tiles: 256 x 256 outputs, 8 waves of 64 x 128 (128 accumulators
 // each), one workgroup per CU (up to 156 KB of LDS); for the last partial
-// round of a launch, quadrants of 128 x 128 on 4 waves, two per CU. With an
-// E4M3 residual (three activation sub-tiles) the stage would not fit three
-// deep, so that variant uses 128 x 256 tiles (8 waves of 32 x 128) and
-// 64 x 128 quadrants.
+// round of a launch, halves of 128 x 256 on 8 waves of 32 x 128, one per
+// CU, or quadrants of 128 x 128 on 4 waves, two per CU. With an E4M3
+// residual (three activation sub-tiles) the stage would not fit three deep,
+// so that variant uses 128 x 256 tiles (8 waves of 32 x 128) and 64 x 128
+// quadrants.
 template <class F, bool kNarrow = (F::kSubA > 2)>
 struct Tiles {
   using Big = TileCfg<256, 256, 8, 1, F>;
   using Quad = TileCfg<128, 128, 4, 2, F>;
+  using Half = TileCfg<128, 256, 8, 1, F>;   // upper or lower half of a big tile
+  static constexpr bool kHasHalf = true;
 };
 template <class F>
 struct Tiles<F, true> {
   using Big = TileCfg<128, 256, 8, 1, F>;
   using Quad = TileCfg<64, 128, 4, 2, F>;
+  using Half = Big;                          // (not used)
+  static constexpr bool kHasHalf = false;
 };
 
 struct GemmParams {
@@ -171,11 +178,12 @@ struct GemmParams {
   int32_t M, N, K;
   // Tile map: `grid` work items; tiles of gm x gn form a tiles_m x tiles_n
   // grid walked in a fixed logical order; item ids map to logical tile
-  // first + (0 .. grid - 1), or with `quadrants` to quadrant (id % 4) of
-  // logical tile first + id / 4. The launch has `wg` workgroups; workgroup b
-  // runs items b, b + wg, b + 2 wg, ... back to back.
+  // first + (0 .. grid - 1), or, split into `pieces` (4: quadrants, 2: upper
+  // and lower halves), to piece id % pieces of logical tile first + id /
+  // pieces. The launch has `wg` workgroups; workgroup b runs items b,
+  // b + wg, b + 2 wg, ... back to back.
   int32_t tiles_m, tiles_n, gm, gn;
-  int32_t first, grid, quadrants, wg;
+  int32_t first, grid, pieces, wg;
   int32_t vec_out;   // Y base and row stride allow 4-element vector stores
 };
 
@@ -239,16 +247,21 @@ __device__ __forceinline__ void tile_origin(const GemmParams& p, int bid, int& m
   const int xcd = bid % 8, idx = bid / 8;
   const int base = total / 8, rem = total % 8;
   const int local = xcd < rem ? xcd * (base + 1) + idx : rem * (base + 1) + (xcd - rem) * base + idx;
-  const int logical = p.first + (p.quadrants ? local / 4 : local);
-  const int q = p.quadrants ? local % 4 : 0;
+  const int logical = p.first + local / p.pieces;
+  const int q = local % p.pieces;
   const int per_group = kGroupM * p.tiles_n;
   const int group = logical / per_group;
   const int first_m = group * kGroupM;
   const int gsize = min(p.tiles_m - first_m, kGroupM);
   const int in_group = logical - group * per_group;
   const int tm = first_m + in_group % gsize, tn = in_group / gsize;
-  m0 = tm * p.gm + (q / 2) * (p.gm / 2);
-  n0 = tn * p.gn + (q % 2) * (p.gn / 2);
+  if (p.pieces == 4) {
+    m0 = tm * p.gm + (q / 2) * (p.gm / 2);
+    n0 = tn * p.gn + (q % 2) * (p.gn / 2);
+  } else {
+    m0 = tm * p.gm + q * (p.gm / 2);
+    n0 = tn * p.gn;
+  }
 }
 
 // The MFMA operand of one activation term for fragment row group i: an E2M1
@@ -793,28 +806,48 @@ hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipSt
   return hipGetLastError();
 }
 
-// Plans the launch: big tiles, one workgroup per CU. When the tile count
-// leaves a last partial round that split into quadrants (two quadrant
-// workgroups per CU) finishes sooner, the whole rounds go out as big tiles
-// and the rest as quadrants in a second launch.
+// Plans the launch: big tiles, one workgroup per CU, in whole rounds of
+// `cus` tiles; a last partial round of `rest` tiles goes out in whichever of
+// these shapes is priced lowest (in units of one big-tile round):
+//  - big tiles on `rest` CUs: 1;
+//  - quadrants (128 x 128 on 4 waves, two workgroups per CU): kQuadRound per
+//    ceil(4 rest / (2 cus)) rounds;
+//  - halves (128 x 256 on 8 waves, one per CU): kHalfRound per
+//    ceil(2 rest / cus) rounds.
+// Quadrants and halves run in a second launch after the whole rounds. The
+// prices are measured: on the 4096 x 13824 x 5120 layer (96 tiles left after
+// three rounds) 384 quadrants took 0.55 of a big round and 192 halves 0.44;
+// on 2048 x 4096 x 4096 (128 tiles, no whole round) one round of halves ran
+// in 0.70 of the big-tile time and of quadrants in 0.84. Halves have the
+// 8-wave workgroup's operand reuse (half the fragment reads per MFMA of a
+// 4-wave quadrant) and fill one CU each.
+constexpr double kQuadRound = 0.55;
+constexpr double kHalfRound = 0.48;
+
 template <class F, bool kOutBf16>
 hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) {
   using Big = typename Tiles<F>::Big;
   using Quad = typename Tiles<F>::Quad;
+  using Half = typename Tiles<F>::Half;
   p.gm = Big::kBM;
   p.gn = Big::kBN;
   p.tiles_m = (p.M + p.gm - 1) / p.gm;
   p.tiles_n = (p.N + p.gn - 1) / p.gn;
   const int tiles = p.tiles_m * p.tiles_n;
   const int rounds = tiles / cus, rest = tiles % cus;
-  // time in units of one big-tile round: a quadrant is a quarter of the work
-  // at half a CU, so a round of 2 * cus quadrants takes half a big round
-  const double all_big = rounds + (rest ? 1.0 : 0.0);
-  const double split = rounds + 0.5 * ((4 * rest + 2 * cus - 1) / (2 * cus));
-  const int big = (rest != 0 && split < all_big) ? rounds * cus : tiles;
+  enum { kTailBig = 1, kTailQuad = 2, kTailHalf = 3 };
+  int tail = kTailBig;
+  if (rest != 0) {
+    const double t_quad = kQuadRound * ((4 * rest + 2 * cus - 1) / (2 * cus));
+    const double t_half = Tiles<F>::kHasHalf ? kHalfRound * ((2 * rest + cus - 1) / cus) : 1e30;
+    double best = 1.0;
+    if (t_quad < best) { best = t_quad; tail = kTailQuad; }
+    if (t_half < best) { best = t_half; tail = kTailHalf; }
+  }
+  const int big = tail == kTailBig ? tiles : rounds * cus;
   p.first = 0;
   p.grid = big;
-  p.quadrants = 0;
+  p.pieces = 1;
   // When every tile lies inside Y and Y takes vector stores, one workgroup
   // per CU streams its tiles back to back; otherwise every tile gets its own
   // workgroup.
@@ -823,9 +856,13 @@ hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) 
   hipError_t e = launch_tiles<Big, F, kOutBf16, true>(p, fast, stream_tiles, stream);
   if (e != hipSuccess || big == tiles) return e;
   p.first = big;
-  p.grid = 4 * (tiles - big);
-  p.quadrants = 1;
-  p.wg = p.grid;
+  if (tail == kTailHalf) {
+    p.pieces = 2;
+    p.grid = p.wg = 2 * (tiles - big);
+    return launch_tiles<Half, F, kOutBf16, false>(p, fast, false, stream);
+  }
+  p.pieces = 4;
+  p.grid = p.wg = 4 * (tiles - big);
   return launch_tiles<Quad, F, kOutBf16, false>(p, fast, false, stream);
 }
 
