@@ -820,9 +820,13 @@ hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipSt
 // on 2048 x 4096 x 4096 (128 tiles, no whole round) one round of halves ran
 // in 0.70 of the big-tile time and of quadrants in 0.84. Halves have the
 // 8-wave workgroup's operand reuse (half the fragment reads per MFMA of a
-// 4-wave quadrant) and fill one CU each.
-constexpr double kQuadRound = 0.55;
-constexpr double kHalfRound = 0.48;
+// 4-wave quadrant) and fill one CU each. The same holds for plain W4A4 and
+// W4A8. The bf16 mode of the backward products is the other way round: its
+// stages are short (32 K elements), and two quadrant workgroups per CU hide
+// each other's barriers better (dX on the 4096 x 5120 x 13824 layer: 554-558
+// us with quadrants, 595-599 us with halves; dW 892-896 against 909-912 us).
+constexpr double kQuadRound = 0.55, kHalfRound = 0.48;
+constexpr double kQuadRoundBf16 = 0.50, kHalfRoundBf16 = 0.60;
 
 template <class F, bool kOutBf16>
 hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) {
@@ -838,8 +842,10 @@ hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) 
   enum { kTailBig = 1, kTailQuad = 2, kTailHalf = 3 };
   int tail = kTailBig;
   if (rest != 0) {
-    const double t_quad = kQuadRound * ((4 * rest + 2 * cus - 1) / (2 * cus));
-    const double t_half = Tiles<F>::kHasHalf ? kHalfRound * ((2 * rest + cus - 1) / cus) : 1e30;
+    const double quad_round = F::kBf16 ? kQuadRoundBf16 : kQuadRound;
+    const double half_round = F::kBf16 ? kHalfRoundBf16 : kHalfRound;
+    const double t_quad = quad_round * ((4 * rest + 2 * cus - 1) / (2 * cus));
+    const double t_half = Tiles<F>::kHasHalf ? half_round * ((2 * rest + cus - 1) / cus) : 1e30;
     double best = 1.0;
     if (t_quad < best) { best = t_quad; tail = kTailQuad; }
     if (t_half < best) { best = t_half; tail = kTailHalf; }

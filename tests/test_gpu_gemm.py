@@ -188,8 +188,9 @@ def test_output_row_stride(out_dtype, ldy, offset):
 @pytest.mark.parametrize("M,N,K", [(4100, 4200, 1024), (4100, 4200, 640), (2304, 7000, 512)])
 def test_two_launch_split_sampled(M, N, K):
     """Shapes whose 256 x 256 tile count leaves a partial last round: whole
-    rounds run as big tiles and the rest as quadrants, with partial edge
-    tiles in both; sampled rows x columns against the oracle (fp32 out)."""
+    rounds run as big tiles and the rest as upper and lower halves, with
+    partial edge tiles in both (the last tile row's lower halves lie wholly
+    past M); sampled rows x columns against the oracle (fp32 out)."""
     rng = np.random.default_rng(M + N + K)
     xb = heavy(rng, M, K)
     wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
