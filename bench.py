@@ -320,10 +320,10 @@ def main():
     gemm_ms = float(gemm_times.mean())
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def batch_ms(fn, reps):
+    def batch_ms(fn, reps, warm=3):
         # back-to-back launches between two events: the per-launch time
         # without an event between launches
-        for _ in range(3):
+        for _ in range(warm):
             fn()
         e0.record(stream)
         for _ in range(reps):
@@ -546,13 +546,16 @@ def main():
         def q5_step():
             rfq._lib.check(lib.rfq_residual_quantize(x5.data_ptr(), 0, c5.M, c5.K, c5.K, q5[0].data_ptr(),
                                                      s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
-        q5_ms = batch_ms(q5_step, 20)
+        # (each pass gets 20 untimed launches first: the first few dozen
+        # launches of a new kernel on this 1.4 GB working set run up to 20%
+        # slower than the steady state)
+        q5_ms = batch_ms(q5_step, 40, warm=20)
         gbs = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5_ms * 1e-3) / 1e9
 
         def q5_rot():
             rfq._lib.check(lib.rfq_rotate_residual_quantize(x5.data_ptr(), 0, c5.M, c5.K, c5.K, q5[0].data_ptr(),
                                                             s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
-        q5r_ms = batch_ms(q5_rot, 20)
+        q5r_ms = batch_ms(q5_rot, 40, warm=20)
         gbs_rot = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5r_ms * 1e-3) / 1e9
         if not args.no_sweep and "dit_ffn_down" not in sweep:
             w5q, w5s = rfq.quantize_mxfp4(to_dev(workloads.w_bf16(c5)))
