@@ -203,12 +203,15 @@ def test_two_launch_split_sampled(M, N, K):
     check_y(y[np.ix_(rows, cols)], y_ref, s_ref, torch.float32, f"split {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K,out_dtype", [(4096, 12288, 512, torch.float32), (4096, 8192, 1024, torch.bfloat16)])
+@pytest.mark.parametrize("M,N,K,out_dtype", [(4096, 12288, 512, torch.float32), (4096, 8192, 1024, torch.bfloat16),
+                                               (4096, 8448, 512, torch.bfloat16)])
 def test_streamed_tiles_every_output(M, N, K, out_dtype):
     """M and N multiples of 256 with two or three whole rounds of tiles on
     256 CUs: each workgroup computes its tiles back to back, fetching the
     next tile's first stages while it finishes the previous one (with K =
-    512 every scale group starts a new tile). Every output checked."""
+    512 every scale group starts a new tile). 4096 x 8448 has 528 tiles:
+    two streamed rounds, then 16 tiles as 32 halves in a second launch.
+    Every output checked."""
     rng = np.random.default_rng(M + N + K + 7)
     xb = heavy(rng, M, K)
     wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
