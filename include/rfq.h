@@ -45,7 +45,8 @@
  *     returns RFQ_ERR_HIP with the HIP error text in the detail string.
  *   - Shapes: rows/M, N may be 0 (then nothing is done and RFQ_OK returned);
  *     K must be positive, a multiple of 32 and at most 2^22; rows, M and N
- *     below 2^31; rows * K, M * K and N * K below 2^37.
+ *     below 2^31; rows * K, M * K and N * K below 2^37; for a GEMM output
+ *     Y [M, N], M * N below 2^40.
  *   - Alignment: X and every code pointer 16-byte aligned, and ldx a
  *     multiple of 8 elements for bf16 X or 4 for fp32 X (so every X row
  *     starts 16-byte aligned); Y

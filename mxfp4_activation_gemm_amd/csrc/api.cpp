@@ -18,6 +18,7 @@ thread_local std::string g_detail;
 constexpr int64_t kMaxK = int64_t(1) << 22;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxElems = int64_t(1) << 37;
+constexpr int64_t kMaxOutputs = int64_t(1) << 40;
 
 rfq_status_t fail(rfq_status_t st, const char* fmt, ...) {
   char buf[256];
@@ -43,6 +44,14 @@ rfq_status_t check_rows_k(int64_t rows, int64_t K, const char* rname) {
   if (K <= 0 || K % 32 != 0 || K > kMaxK)
     return fail(RFQ_ERR_INVALID_SHAPE, "K = %lld must be positive, a multiple of 32 and at most 2^22", (long long)K);
   if (rows * K >= kMaxElems) return fail(RFQ_ERR_INVALID_SHAPE, "%s * K = %lld exceeds 2^37", rname, (long long)(rows * K));
+  return RFQ_OK;
+}
+
+// A GEMM output Y [M, N] holds fewer than 2^40 elements (the tile count
+// stays in 32-bit arithmetic).
+rfq_status_t check_mn(int64_t M, int64_t N) {
+  if (M > 0 && N > 0 && M > (kMaxOutputs - 1) / N)
+    return fail(RFQ_ERR_INVALID_SHAPE, "M * N = %lld x %lld reaches 2^40", (long long)M, (long long)N);
   return RFQ_OK;
 }
 
@@ -128,6 +137,7 @@ rfq_status_t gemm_common(int x_fmt, int r_fmt, const uint8_t* qx_codes, const ui
                          rfq_stream_t stream) {
   RFQ_TRY(check_rows_k(M, K, "M"));
   RFQ_TRY(check_rows_k(N, K, "N"));
+  RFQ_TRY(check_mn(M, N));
   if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
     return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
   if (M == 0 || N == 0) return ok();
@@ -216,6 +226,7 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                         void* workspace, size_t workspace_bytes, rfq_stream_t stream) {
   RFQ_TRY(check_rows_k(M, K, "M"));
   RFQ_TRY(check_rows_k(N, K, "N"));
+  RFQ_TRY(check_mn(M, N));
   RFQ_TRY(check_dtype(x_dtype));
   if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
     return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);

@@ -91,6 +91,7 @@ def test_gemm_validation(lib):
     assert g(lib, y=None) == "RFQ_ERR_NULL_POINTER"
     assert g(lib, K=40) == "RFQ_ERR_INVALID_SHAPE"
     assert g(lib, N=-3) == "RFQ_ERR_INVALID_SHAPE"
+    assert g(lib, M=1 << 20, N=1 << 20, K=32) == "RFQ_ERR_INVALID_SHAPE"   # Y of 2^40 elements
     assert g(lib, yd=7) == "RFQ_ERR_UNSUPPORTED_DTYPE"
     assert g(lib, ldy=4) == "RFQ_ERR_INVALID_STRIDE"
     assert g(lib, y=FAKE + 1, yd=0) == "RFQ_ERR_MISALIGNED"
