@@ -211,7 +211,7 @@ def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=No
                         "one 8-wave workgroup per CU (rfq_probe_mfma_ceiling_e4m3)"}
     return {"TFLOP_per_s": round(tf, 1), "pct_of_datasheet_peak": round(100 * tf / FP4_PEAK_TFLOPS, 2),
             "shader_clock_GHz": round(clock, 3),
-            "what": "scaled FP4 MFMA loop on this workload's Q(X)/Q(R) and W codes, no memory traffic, "
+            "what": "scaled FP4 16x16x128 MFMA loop (the GEMM's instruction) on this workload's Q(X)/Q(R) and W codes, no memory traffic, "
                     "one 8-wave workgroup per CU (rfq_probe_mfma_ceiling)"}
 
 

@@ -5,9 +5,10 @@
  * MFMA issue rate: with real operand data the shader clock drops well below
  * its 2.4 GHz peak. This probe measures that ceiling directly, as the rate of
  * a loop that does nothing but issue the GEMM's instruction
- * (v_mfma_scale_f32_32x32x64_f8f6f4, both operands FP4) on operand bytes the
- * caller supplies, with no memory traffic in the loop. The GEMM's throughput
- * is then reported against both the datasheet peak and this ceiling.
+ * (v_mfma_scale_f32_16x16x128_f8f6f4 with both operands FP4, the form the
+ * E2M1 x E2M1 GEMMs use) on operand bytes the caller supplies, with no
+ * memory traffic in the loop. The GEMM's throughput is then reported
+ * against both the datasheet peak and this ceiling.
  */
 #ifndef RFQ_PROBE_H_
 #define RFQ_PROBE_H_
@@ -24,8 +25,8 @@ extern "C" {
 /*
  * rfq_probe_mfma_ceiling - launch `workgroups` workgroups of 512 threads
  * (two waves per SIMD, as the GEMM runs; launch one per CU), each running
- * `iters` iterations of 32 FP4 scaled MFMAs per wave over 8 independent
- * accumulators. Each lane loads four 16-byte operands from each buffer once,
+ * `iters` iterations of 64 FP4 scaled 16 x 16 x 128 MFMAs per wave over 32
+ * independent accumulators. Each lane loads four 16-byte operands from each buffer once,
  * before the loop, at consecutive 16-byte positions taken modulo the buffer
  * size, so any buffer of at least 16 bytes serves.
  *   a_codes, a_bytes: bytes of the first operand (e.g. Q(X) and Q(R) codes);
@@ -37,17 +38,20 @@ extern "C" {
  *   sink: device buffer of 512 * workgroups floats (out): accumulator sums,
  *     written so that the loop is not optimised away.
  * Flops per call: 2 * 32 * 32 * 64 * 32 * 8 * iters * workgroups (8 waves of
- * 32 MFMAs per iteration). Asynchronous on `stream`; errors as in rfq.h.
+ * 64 MFMAs of 2 * 16 * 16 * 128 flops per iteration). Asynchronous on
+ * `stream`; errors as in rfq.h.
  */
 rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
                                     int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream);
 
 /*
- * rfq_probe_mfma_ceiling_e4m3 - the same loop with the second operand in
- * E4M3 (the instruction of the MXFP8 activation variants: MXFP4 weight first,
- * MXFP8 activation second). Each lane loads eight 16-byte pieces of b_codes
- * (two per operand, 32 bytes) at consecutive positions modulo its size; all
- * else as rfq_probe_mfma_ceiling, including the flop count per call.
+ * rfq_probe_mfma_ceiling_e4m3 - the same measurement for the instruction of
+ * the MXFP8 activation variants, v_mfma_scale_f32_32x32x64_f8f6f4 with the
+ * MXFP4 weight first and the E4M3 activation second: 32 MFMAs per wave per
+ * iteration over 8 accumulators. Each lane loads eight 16-byte pieces of
+ * b_codes (two per operand, 32 bytes) at consecutive positions modulo its
+ * size; all else as rfq_probe_mfma_ceiling, including the flop count per
+ * call.
  */
 rfq_status_t rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes,
                                          size_t b_bytes, int workgroups, int iters, uint64_t* stamps, float* sink,

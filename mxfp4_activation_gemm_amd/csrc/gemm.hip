@@ -7,19 +7,22 @@
 // i.e. one contraction of [QX | QR] (M x 2K) against [W ; W] over a doubled
 // K, every term landing in the same fp32 accumulator.
 //
-// Instruction: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands FP4
-// (E2M1). Operand lane layout (checked on hardware): lane l holds row l % 32
-// and the 32 elements of K-block l / 32 of the 64-wide K step, as 16 bytes,
-// element 2j in the low nibble of byte j; its 32-bit scale operand supplies
-// the E8M0 code of that (row, block) in the byte chosen by op_sel. Output
-// lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4. W is the
-// first operand and X (or R) the second, so an output tile is a tile of Y^T:
-// each lane holds one row of Y and, per group of four accumulators, four
+// Instruction: the scaled MFMA v_mfma_scale_f32_*_f8f6f4. E2M1 x E2M1
+// products (RFQ, plain W4A4) use its 16 x 16 x 128 form (lane layout and the
+// reason at mfma16_group below); E4M3 activations use the 32 x 32 x 64 form:
+// lane l holds row l % 32 and K-block l / 32 of the 64-wide K step (E2M1: 16
+// bytes, element 2j in the low nibble of byte j; E4M3: see Fmts), its 32-bit
+// scale operand supplies the E8M0 code of that (row, block) in the byte
+// chosen by op_sel, and output lane l holds column l % 32, rows
+// 8 (i / 4) + 4 (l / 32) + i % 4 (checked on hardware). W is the first
+// operand and X (or R) the second, so an output tile is a tile of Y^T: each
+// lane holds one row of Y and, per group of four accumulators, four
 // consecutive columns, which leave as one vector store.
 //
 // Tiling: a 256 x 256 output tile per workgroup of 8 waves on a 4 x 2 grid
 // (two waves per SIMD, one workgroup per CU); each wave owns 64 x 128
-// outputs = 2 x 4 MFMA tiles (128 fp32 accumulators per lane). K advances
+// outputs = 4 x 8 tiles of 16 x 16, or 2 x 4 of 32 x 32 (128 fp32
+// accumulators per lane either way). K advances
 // 128 elements (64 bytes of codes per row) per stage, as two MFMA steps of
 // 64. When the tile count leaves a last partial round on the CUs, that
 // round's tiles are split, in a second launch, into upper and lower halves
@@ -109,6 +112,9 @@ struct Fmts {
   static constexpr int kScalesA = kBf16 ? 0 : (kResid ? 2 : 1);   // activation scale streams
   static constexpr int kScalesB = kBf16 ? 0 : 1;       // weight scale stream
   static constexpr int kTerms = kResid ? 2 : 1;        // MFMAs per output tile per step
+  // E2M1 x E2M1 products run on the 16 x 16 x 128 form of the scaled MFMA
+  // (see the kernel); E4M3 and bf16 operands on the 32 x 32 forms.
+  static constexpr bool kM16 = kX == 4 && (kR == 0 || kR == 4);
   static_assert((kX == 4 && (kR == 0 || kR == 4 || kR == 8)) || (kX == 8 && kR == 0) ||
                     (kX == 16 && (kR == 0 || kR == 16)),
                 "formats");
@@ -134,6 +140,7 @@ struct TileCfg {
   static constexpr int kWavesM = kWaves / kWavesN;
   static constexpr int kWaveM = kBM / kWavesM, kWaveN = kBN / kWavesN;
   static constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;           // MFMA tiles per wave
+  static constexpr int kT16M = kWaveM / 16, kT16N = kWaveN / 16;       // the same in 16 x 16 tiles
   static constexpr int kTileBytesA = kBM * kRowBytes, kTileBytesB = kBN * kRowBytes;   // one sub-tile
   static constexpr int kStageBytes = F::kSubA * kTileBytesA + kTileBytesB;
   static constexpr int kScaleBytesA = kBM * kScaleRowBytes;
@@ -142,6 +149,7 @@ struct TileCfg {
   static constexpr int kLoadsA = kBM / 16 / kWaves;    // 16-row DMA instructions per wave per sub-tile of X / R
   static constexpr int kLoadsB = kBN / 16 / kWaves;    // for W
   static_assert(kTM >= 1 && kTN >= 1 && kLoadsA >= 1 && kLoadsB >= 1, "tile shape");
+  static_assert(!F::kM16 || (kT16M % 2 == 0 && kT16N % 2 == 0), "16 x 16 tiles come in halves");
   static_assert(kLdsBytes * kOcc <= 160 * 1024, "LDS budget per CU");
 };
 // Main tiles: 256 x 256 outputs, 8 waves of 64 x 128 (128 accumulators
@@ -330,6 +338,49 @@ __device__ __forceinline__ void interleave_hint() {
   interleave_slots<0, kMfma, kVmem, kReads>();
 }
 
+// The 16 x 16 x 128 form of the instruction, for E2M1 x E2M1 (lane layout
+// checked on hardware with random operands and per-lane scales): lane l
+// holds row l % 16 and the 32 elements of K-block l / 16 of the 128-wide
+// step (16 bytes, element 2j in the low nibble of byte j), and its scale
+// operand supplies that (row, block)'s E8M0 code in the byte op_sel picks;
+// output lane l holds column l % 16, rows 4 (l / 16) + 0..3. A stage (128 K
+// elements) is one step. On this workload's codes its power-limited rate
+// measured 13% above the 32 x 32 x 64 form's (7.45 against 6.6 PFLOP/s in
+// an MFMA-only loop): a quarter of the accumulator reads and writes per
+// instruction for half the products.
+//
+// A lane's scale bytes for the four stages of a scale group, gathered from
+// its row's 16 group bytes (stage s's four blocks at bytes 4 s .. 4 s + 3)
+// into one word whose byte s is the lane's block (lane / 16) of stage s;
+// sel01 = b | (4 + b) << 8 for that block b. (Elements are copied to
+// scalars first: a bit cast of an ext-vector element has been seen to read
+// element 0.)
+__device__ __forceinline__ uint32_t gather_stage_bytes(i32x4_t w, uint32_t sel01) {
+  const int e0 = w.x, e1 = w.y, e2 = w.z, e3 = w.w;
+  const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)e1, (uint32_t)e0, sel01);
+  const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)e3, (uint32_t)e2, sel01);
+  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+
+// One group of 16 x 16 x 128 MFMAs: weight half HW (kHN fragments of 16
+// rows) against activation half HX (kHM row tiles, kTerms terms each), at
+// stage P of the scale group (the scale byte op_sel picks). Terms outermost,
+// so MFMAs into one accumulator are kHM x kHN instructions apart.
+template <int P, int HW, int HX, int kTerms, int kHM, int kHN, int kT16M, int kT16N>
+__device__ __forceinline__ void mfma16_group(f32x4_t (&acc)[kT16M][kT16N], const i32x4_t (&wf)[2][kHN],
+                                             const i32x4_t (&xf)[2][kHM * kTerms], const uint32_t (&ws)[2][kHN],
+                                             const uint32_t (&xs)[2][kHM * kTerms]) {
+#pragma unroll
+  for (int t = 0; t < kTerms; ++t)
+#pragma unroll
+    for (int m = 0; m < kHM; ++m)
+#pragma unroll
+      for (int n = 0; n < kHN; ++n)
+        acc[HX * kHM + m][HW * kHN + n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            widen(wf[HW][n]), widen(xf[HX][m * kTerms + t]), acc[HX * kHM + m][HW * kHN + n], 4, 4, P,
+            (int)ws[HW][n], P, (int)xs[HX][m * kTerms + t]);
+}
+
 // kFast: K % 512 == 0 (whole stages and whole 16-block scale groups); the
 // other instantiation masks partial K and waits for all loads at each stage.
 // kStream (needs kFast): every tile of the launch lies inside Y and Y takes
@@ -339,6 +390,7 @@ template <class C, class F, bool kOutBf16, bool kFast, bool kStream>
 __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParams p) {
   static_assert(kFast || !kStream, "streaming needs whole scale groups");
   constexpr bool kResid = F::kResid;
+  constexpr bool kM16 = F::kM16;
   constexpr int kSubA = F::kSubA;
   constexpr int kBM = C::kBM, kBN = C::kBN, kWaves = C::kWaves;
   constexpr int kWaveM = C::kWaveM, kWaveN = C::kWaveN, kTM = C::kTM, kTN = C::kTN;
@@ -548,14 +600,86 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
                                                 8 * pair);
   };
 
+  // 16 x 16 x 128 path: fragments and scale words in two halves each (the
+  // weight's kT16N row tiles, the activation's kT16M row tiles with their
+  // terms). A stage's MFMAs go in four groups, (W0, A0), (W0, A1), (W1, A0),
+  // (W1, A1), and each half is re-read for the next stage right after its
+  // last use in this one: W0 after the second group (past the barrier, where
+  // the next stage has landed), A0 after the third, W1 and A1 after the
+  // fourth (during the next stage's first group). So one set of fragment
+  // registers serves, as in the 32 x 32 path. Scale words hold a whole
+  // scale group (byte s = stage s) and roll over at its last stage the same
+  // way.
+  constexpr int kHM = C::kT16M / 2, kHN = C::kT16N / 2;
+  constexpr int kXH = kHM * F::kTerms;          // activation fragments per half
+  i32x4_t wf[2][kHN], xf[2][kXH];
+  uint32_t ws[2][kHN], xs[2][kXH];
+  // lane offset of a 16-row fragment: row lane % 16, chunk lane / 16
+  // (swizzled by the row; fragment bases are multiples of 16 rows)
+  const uint32_t rd16 = (lane & 15) * kRowBytes + 16 * ((lane >> 4) ^ swz(lane & 15));
+  const uint32_t sel01 = (lane >> 4) | ((4 + (lane >> 4)) << 8);
+  auto read_w16 = [&](int st, auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    uint32_t off = rd16;
+    asm volatile("" : "+v"(off));
+    const uint8_t* buf = ring + (st % kRing) * kStageBytes + kSubA * kTileBytesA + off;
+#pragma unroll
+    for (int n = 0; n < kHN; ++n) wf[h][n] = read_frag(buf + (b_row0 + 16 * (h * kHN + n)) * kRowBytes);
+  };
+  auto read_x16 = [&](int st, auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    uint32_t off = rd16;
+    asm volatile("" : "+v"(off));
+    const uint8_t* buf = ring + (st % kRing) * kStageBytes + off;
+#pragma unroll
+    for (int m = 0; m < kHM; ++m)
+#pragma unroll
+      for (int t = 0; t < F::kTerms; ++t)
+        xf[h][m * F::kTerms + t] = read_frag(buf + t * kTileBytesA + (a_row0 + 16 * (h * kHM + m)) * kRowBytes);
+  };
+  auto read_ws16 = [&](auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    if constexpr (!F::kBf16) {
+#pragma unroll
+      for (int n = 0; n < kHN; ++n) {
+        const uint32_t row = b_row0 + 16 * (h * kHN + n) + (lane & 15);
+        ws[h][n] = gather_stage_bytes(
+            *reinterpret_cast<const i32x4_t*>(sbuf + F::kScalesA * kScaleBytesA + row * kScaleRowBytes), sel01);
+      }
+    }
+  };
+  auto read_xs16 = [&](auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    if constexpr (!F::kBf16) {
+#pragma unroll
+      for (int m = 0; m < kHM; ++m) {
+        const uint32_t row = a_row0 + 16 * (h * kHM + m) + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < F::kTerms; ++t)
+          xs[h][m * F::kTerms + t] = gather_stage_bytes(
+              *reinterpret_cast<const i32x4_t*>(sbuf + t * kScaleBytesA + row * kScaleRowBytes), sel01);
+      }
+    }
+  };
+
   f32x16_t acc[kTM][kTN];
+  f32x4_t acc16[C::kT16M][C::kT16N];
   auto zero_acc = [&]() __attribute__((always_inline)) {
+    if constexpr (kM16) {
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
+      for (int i = 0; i < C::kT16M; ++i)
 #pragma unroll
-      for (int j = 0; j < kTN; ++j)
+        for (int j = 0; j < C::kT16N; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+          for (int q = 0; q < 4; ++q) acc16[i][j][q] = 0.f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    }
   };
   zero_acc();
 
@@ -572,11 +696,52 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   wait_lgkmcnt0();
   stage_barrier();
   i32x4_t a0[kSubA][kTM], bw0[kTN], a1[kSubA][kTM], bw1[kTN];
-  read_scale_pair(0);
-  read_step(0, 0, a0, bw0);
+  if constexpr (kM16) {
+    // stage 0's first halves and the group's first-half scale words; the
+    // second halves are read in stage 0's first group, as in every stage
+    read_ws16(std::integral_constant<int, 0>{});
+    read_xs16(std::integral_constant<int, 0>{});
+    read_w16(0, std::integral_constant<int, 0>{});
+    read_x16(0, std::integral_constant<int, 0>{});
+  } else {
+    read_scale_pair(0);
+    read_step(0, 0, a0, bw0);
+  }
 
   // One stage; P = st % 4 is a compile-time constant so that every wait count
   // and scale-word index below is one.
+  // The middle of stage st: stage st + 1 must have landed, and at the end of
+  // a group also the next group's scales. The only loads issued after those
+  // are stage st + 2's (scales go out before the stage loads of the same
+  // sync point, and every stage issues the same loads, see issue_stage).
+  // After the barrier every wave is past its reads of stage st, so its slot
+  // takes stage st + 3; at P == 2 every wave also holds the group's scale
+  // words for its remaining stages, so the scale buffer takes the next group
+  // (issued first, see the wait).
+  auto sync_and_refill = [&](auto pc, int st) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    if (kFast)
+      wait_vmcnt<kDmaPerStage>();
+    else
+      wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kStream && P == 1 && st + kRing - load_base == nstages && load_tile + 1 < ntiles) {
+      // the stream reaches the next tile with this stage's fetch (stage
+      // st + 3 = 4 g + 4, a tile start; every earlier fetch of the old tile
+      // has been issued, and none of the new one)
+      ++load_tile;
+      load_base += nstages;
+      const GemmParams q = fresh_params();
+      int m0, n0;
+      tile_origin(q, (int)blockIdx.x + load_tile * q.wg, m0, n0);
+      set_load_tile(q, m0, n0);
+    }
+    if (P == 2) issue_scales(st / kScaleGroup + 1);
+    issue_stage(st + kRing, std::integral_constant<int, 0>{});
+  };
+
   auto stage = [&](auto pc, int st) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
     __builtin_amdgcn_sched_barrier(0);   // keep each stage's schedule to itself
@@ -613,33 +778,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     mfma_step<0, F, kTM, kTN>(acc, a0, bw0, cx, cr, cw);
     interleave_hint<kReadsPerStep, kFast ? kDmaPerStage - kPart0 : 0, kMfmaPerStep>();
 
-    // Stage st + 1 must have landed, and at the end of a group also the next
-    // group's scales. The only loads issued after those are stage st + 2's
-    // (scales go out before the stage loads of the same sync point, and
-    // every stage issues the same loads, see issue_stage).
-    if (kFast)
-      wait_vmcnt<kDmaPerStage>();
-    else
-      wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    stage_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // every wave is past its reads of stage st: its slot takes stage st + 3;
-    // at P == 2 every wave also holds the group's last scale words, so the
-    // scale buffer takes the next group (issued first, see the wait above)
-    if (kStream && P == 1 && st + kRing - load_base == nstages && load_tile + 1 < ntiles) {
-      // the stream reaches the next tile with this stage's fetch (stage
-      // st + 3 = 4 g + 4, a tile start; every earlier fetch of the old tile
-      // has been issued, and none of the new one)
-      ++load_tile;
-      load_base += nstages;
-      const GemmParams q = fresh_params();
-      int m0, n0;
-      tile_origin(q, (int)blockIdx.x + load_tile * q.wg, m0, n0);
-      set_load_tile(q, m0, n0);
-    }
-    if (P == 2) issue_scales(st / kScaleGroup + 1);
-    issue_stage(st + kRing, std::integral_constant<int, 0>{});
+    sync_and_refill(pc, st);
 
     // second MFMA step; meanwhile read stage st + 1's first step and, after
     // stages 1 and 3 of a group, the scale words of the next two stages (this
@@ -654,6 +793,53 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // One stage on the 16 x 16 x 128 path: four MFMA groups, the barrier
+  // after the second; the reads beside each group are the halves freed by
+  // the groups before it (see the register note above).
+  auto stage16 = [&](auto pc, int st) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    constexpr int kG = kHM * kHN * F::kTerms;   // MFMAs per group
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    __builtin_amdgcn_sched_barrier(0);
+    // (W0, A0): meanwhile stage st's second halves (and, at a group's first
+    // stage, its second-half scale words) and the second part of stage
+    // st + 2's loads
+    issue_stage(st + kRing - 1, I1{});
+    read_w16(st, I1{});
+    read_x16(st, I1{});
+    if (P == 0) {
+      read_ws16(I1{});
+      read_xs16(I1{});
+    }
+    mfma16_group<P, 0, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    interleave_hint<kHN + kXH + (P == 0 ? kHN + kXH : 0), kFast ? kDmaPerStage - kPart0 : 0, kG>();
+    __builtin_amdgcn_sched_barrier(0);
+    // (W0, A1)
+    mfma16_group<P, 0, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    __builtin_amdgcn_sched_barrier(0);
+    sync_and_refill(pc, st);
+    // (W1, A0): meanwhile stage st + 1's W0 (and at the group's last stage
+    // the next group's W0 scale words)
+    read_w16(st + 1, I0{});
+    if (P == 3) read_ws16(I0{});
+    mfma16_group<P, 1, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    interleave_hint<kHN + (P == 3 ? kHN : 0), kFast ? kPart0 + (P == 2 ? kScaleLoadsPerWave : 0) : 0, kG>();
+    __builtin_amdgcn_sched_barrier(0);
+    // (W1, A1): meanwhile stage st + 1's A0 (and the next group's A0 scale words)
+    read_x16(st + 1, I0{});
+    if (P == 3) read_xs16(I0{});
+    mfma16_group<P, 1, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    interleave_hint<kXH + (P == 3 ? kXH : 0), 0, kG>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run_stage = [&](auto pc, int st) __attribute__((always_inline)) {
+    if constexpr (kM16)
+      stage16(pc, st);
+    else
+      stage(pc, st);
+  };
+
   // Epilogue of a tile: fp32 accumulators to Y. The weight is the MFMA's
   // first operand, so tile (i, j) holds Y^T: lane (lhalf, lrow) has row m of
   // Y and, in accumulator group q / 4, the four consecutive columns
@@ -661,6 +847,50 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // fp32) when the host found Y's base and row stride aligned for it.
   auto store_tile = [&](int em0, int en0) __attribute__((always_inline)) {
     const GemmParams q = fresh_params();
+    if constexpr (kM16) {
+      // 16 x 16 tiles: lane (lane / 16, lane % 16) has row m of Y and the
+      // four consecutive columns 16 n + 4 (lane / 16) + (0..3) of tile n
+      const int row16 = em0 + (int)a_row0 + (int)(lane & 15);
+      const int col16 = en0 + (int)b_row0 + 4 * (int)(lane >> 4);
+#pragma unroll
+      for (int i = 0; i < C::kT16M; ++i) {
+        const int row = row16 + 16 * i;
+        if (row >= q.M) continue;
+#pragma unroll
+        for (int j = 0; j < C::kT16N; ++j) {
+          const int col = col16 + 16 * j;
+          const f32x4_t& a = acc16[i][j];
+          const float v[4] = {a[0], a[1], a[2], a[3]};
+          if (kOutBf16) {
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              uint32_t u = __builtin_bit_cast(uint32_t, v[e]);
+              u = (v[e] != v[e]) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u);
+              h[e] = (uint16_t)(u >> 16);
+            }
+            uint16_t* dst = reinterpret_cast<uint16_t*>(q.y) + (int64_t)row * q.ldy + col;
+            if (q.vec_out && col + 3 < q.N) {
+              *reinterpret_cast<i32x2_t*>(dst) = i32x2_t{(int)(h[0] | ((uint32_t)h[1] << 16)), (int)(h[2] | ((uint32_t)h[3] << 16))};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < q.N) dst[e] = h[e];
+            }
+          } else {
+            float* dst = reinterpret_cast<float*>(q.y) + (int64_t)row * q.ldy + col;
+            if (q.vec_out && col + 3 < q.N) {
+              *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < q.N) dst[e] = v[e];
+            }
+          }
+        }
+      }
+      return;
+    }
     const int row_base = em0 + (int)a_row0 + (int)lrow;
     const int col_base = en0 + (int)b_row0 + 4 * (int)lhalf;
     if constexpr (F::kOutT) {
@@ -742,6 +972,33 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       return;
     }
     const GemmParams q = fresh_params();
+    if constexpr (kM16) {
+#pragma unroll
+      for (int i = 0; i < C::kT16M; ++i) {
+        const int64_t at =
+            (int64_t)(em0 + (int)a_row0 + (int)(lane & 15) + 16 * i) * q.ldy + en0 + (int)b_row0 + 4 * (int)(lane >> 4);
+        uint16_t* yb = reinterpret_cast<uint16_t*>(q.y) + at;
+        float* yf = reinterpret_cast<float*>(q.y) + at;
+#pragma unroll
+        for (int j = 0; j < C::kT16N; ++j) {
+          const f32x4_t& a = acc16[i][j];
+          if (kOutBf16) {
+            uint32_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = a[e];
+              const uint32_t u = __builtin_bit_cast(uint32_t, v);
+              h[e] = ((v != v) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+            }
+            *reinterpret_cast<i32x2_t*>(yb + 16 * j) = i32x2_t{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16))};
+          } else {
+            *reinterpret_cast<f32x4_t*>(yf + 16 * j) = f32x4_t{a[0], a[1], a[2], a[3]};
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const int64_t at = (int64_t)(em0 + (int)a_row0 + (int)lrow + 32 * i) * q.ldy + en0 + (int)b_row0 + 4 * (int)lhalf;
@@ -773,10 +1030,10 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // register allocator needs to fit this loop without spills)
   int comp_base = 0, comp_tile = 0;
   for (int st = 0; st < total_stages; st += kScaleGroup) {
-    stage(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < total_stages) stage(std::integral_constant<int, 1>{}, st + 1);
-    if (st + 2 < total_stages) stage(std::integral_constant<int, 2>{}, st + 2);
-    if (st + 3 < total_stages) stage(std::integral_constant<int, 3>{}, st + 3);
+    run_stage(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < total_stages) run_stage(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < total_stages) run_stage(std::integral_constant<int, 2>{}, st + 2);
+    if (st + 3 < total_stages) run_stage(std::integral_constant<int, 3>{}, st + 3);
     if (kStream && st + kScaleGroup - comp_base == nstages && st + kScaleGroup < total_stages) {
       // a tile ends here and another follows in the stream: store it, then
       // start the next from zero (its first fragments are already read)

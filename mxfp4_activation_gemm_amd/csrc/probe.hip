@@ -1,9 +1,12 @@
 // MFMA issue ceiling under the power limit (measurement probe, not part of
-// the RFQ layer): a loop of the GEMM's scaled MFMA (E2M1 x E2M1, or E2M1 x
-// E4M3 as in the MXFP8 activation variants) on caller-supplied operand bytes, with no memory traffic inside the loop, timed per
-// workgroup in shader-clock cycles (s_memtime) and in 100 MHz constant-clock
-// ticks (s_memrealtime), so that both the rate and the clock it ran at can be
-// read back.
+// the RFQ layer): a loop of the GEMM's scaled MFMA on caller-supplied
+// operand bytes, with no memory traffic inside the loop, timed per workgroup
+// in shader-clock cycles (s_memtime) and in 100 MHz constant-clock ticks
+// (s_memrealtime), so that both the rate and the clock it ran at can be read
+// back. E2M1 x E2M1 runs the 16 x 16 x 128 form the GEMM uses for it (64
+// instructions per wave per iteration over 32 accumulators); E2M1 x E4M3
+// the 32 x 32 x 64 form of the MXFP8 activation variants (32 instructions
+// over 8 accumulators). Both do the same flops per iteration.
 
 #include "kernels.h"
 
@@ -12,6 +15,7 @@ namespace {
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;   // two waves per SIMD, like the GEMM's main tile
@@ -32,25 +36,51 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a
     const i32x4_t lo = b[(2 * slot) % b_n], hi = b[(2 * slot + 1) % b_n];
     rb[i] = kBFmt == 8 ? i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w} : i32x8_t{lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
   }
-  f32x16_t acc[kAcc];
-  for (int q = 0; q < kAcc; ++q)
-    for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
-  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int q = 0; q < kAcc; ++q) {
-        const i32x4_t x = ra[(q + s) & 3];
-        acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(i32x8_t{x.x, x.y, x.z, x.w, 0, 0, 0, 0},
-                                                                 rb[(q / 2 + s) & 3], acc[q], 4, kBFmt == 8 ? 0 : 4,
-                                                                 0, 120 + q, 0, 122);
-      }
-  }
-  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   float sum = 0.f;
-  for (int q = 0; q < kAcc; ++q)
-    for (int e = 0; e < 16; ++e) sum += acc[q][e];
+  uint64_t c0, r0, c1, r1;
+  if constexpr (kBFmt == 8) {
+    f32x16_t acc[kAcc];
+    for (int q = 0; q < kAcc; ++q)
+      for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int q = 0; q < kAcc; ++q) {
+          const i32x4_t x = ra[(q + s) & 3];
+          acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(i32x8_t{x.x, x.y, x.z, x.w, 0, 0, 0, 0},
+                                                                   rb[(q / 2 + s) & 3], acc[q], 4, 0, 0, 120 + q, 0, 122);
+        }
+    }
+    c1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
+    for (int q = 0; q < kAcc; ++q)
+      for (int e = 0; e < 16; ++e) sum += acc[q][e];
+  } else {
+    constexpr int kAcc16 = 4 * kAcc;   // the same accumulator registers as 16 x 16 tiles
+    f32x4_t acc[kAcc16];
+    for (int q = 0; q < kAcc16; ++q)
+      for (int e = 0; e < 4; ++e) acc[q][e] = 0.f;
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int q = 0; q < kAcc16; ++q) {
+          const i32x4_t x = ra[(q + s) & 3];
+          acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(i32x8_t{x.x, x.y, x.z, x.w, 0, 0, 0, 0},
+                                                                    rb[(q / 8 + s) & 3], acc[q], 4, 4, 0, 120 + (q & 7), 0,
+                                                                    122);
+        }
+    }
+    c1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
+    for (int q = 0; q < kAcc16; ++q)
+      for (int e = 0; e < 4; ++e) sum += acc[q][e];
+  }
   sink[blockIdx.x * kThreads + t] = sum;
   if (t == 0) {
     stamps[2 * blockIdx.x] = c1 - c0;
