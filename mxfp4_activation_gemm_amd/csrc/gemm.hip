@@ -220,8 +220,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+// soff: a wave-uniform byte offset added to every lane's (it goes in the
+// instruction's scalar offset, not in the lanes' offset registers)
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, (int)soff, 0, 0);
 }
 
 __device__ __forceinline__ i32x4_t read_frag(const uint8_t* p) { return *reinterpret_cast<const i32x4_t*>(p); }
@@ -482,15 +484,20 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   constexpr int kScaleLoadsPerWave = (kPieces + kWaves - 1) / kWaves;   // 0 without scales
 
   // Stream stage st (stage st - load_base of the tile being fetched). A
-  // stage past the end of the stream is still issued, at an out-of-range
-  // offset: it writes zeros into a slot nothing reads again, and keeps the
-  // number of loads per stage constant. The loads go out in two parts.
+  // stage past the end of the stream is still issued, so that the number of
+  // loads per stage stays constant; it fills a slot nothing reads again. In
+  // the kFast variant a stage's K offset is the loads' scalar offset and each
+  // lane's offset is the same in every stage (no per-stage lane arithmetic),
+  // and a stage past the end re-reads the tile's stage 0; otherwise the lane
+  // offsets carry the stage and a chunk past K, or a stage past the end, is
+  // aimed out of range (zeros). The loads go out in two parts.
   constexpr int kPart0 = (kDmaPerStage + 1) / 2;
   auto issue_stage = [&](int st, auto part_c) __attribute__((always_inline)) {
     constexpr int part = decltype(part_c)::value;   // 0: first kPart0 loads, 1: the rest, 2: all
     uint8_t* buf = ring + (st % kRing) * kStageBytes;
     const int kst = st - load_base;
     const bool past_end = st >= total_stages;
+    const uint32_t kst_s = past_end ? 0u : (uint32_t)kst;   // kFast: stage in the scalar offset
 #pragma unroll
     for (int n = 0; n < C::kLoadsA; ++n) {
       uint8_t* dst = buf + (kBM / kWaves * wave + 16 * n) * kRowBytes;
@@ -502,20 +509,29 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
         // K-block (within the stage) of this lane's chunk: c for E2M1; for
         // E4M3 2 (c / 2), + 1 in the second sub-tile
         const uint32_t blk = fp8 ? 2 * (lda_chunk[n] >> 1) + (second ? 1 : 0) : lda_chunk[n];
-        uint32_t vo = fp8 ? lda_voff(std::integral_constant<int, 8>{}, n) + (uint32_t)kst * (2 * kRowBytes)
-                          : lda_voff(std::integral_constant<int, 4>{}, n) + (uint32_t)kst * kRowBytes;
-        if ((!kFast && (uint32_t)kst * (kBK / 32) + blk >= kblocks) || past_end) vo = kOOB;
+        const uint32_t base = fp8 ? lda_voff(std::integral_constant<int, 8>{}, n) : lda_voff(std::integral_constant<int, 4>{}, n);
+        const uint32_t step = fp8 ? 2 * kRowBytes : kRowBytes;
+        uint32_t vo = base, so = kst_s * step;
+        if (!kFast) {
+          vo = base + (uint32_t)kst * step;
+          so = 0;
+          if ((uint32_t)kst * (kBK / 32) + blk >= kblocks || past_end) vo = kOOB;
+        }
         const int ix = kSubA * n + t;
-        if (part == 2 || (ix < kPart0) == (part == 0)) load16_to_lds(ra[t], dst + t * kTileBytesA, vo);
+        if (part == 2 || (ix < kPart0) == (part == 0)) load16_to_lds(ra[t], dst + t * kTileBytesA, vo, so);
       }
     }
 #pragma unroll
     for (int n = 0; n < C::kLoadsB; ++n) {
-      uint32_t vo = ldb_voff[n] + (uint32_t)kst * kRowBytes;
-      if ((!kFast && (uint32_t)kst * (kBK / 32) + ldb_chunk[n] >= kblocks) || past_end) vo = kOOB;
+      uint32_t vo = ldb_voff[n], so = kst_s * kRowBytes;
+      if (!kFast) {
+        vo = ldb_voff[n] + (uint32_t)kst * kRowBytes;
+        so = 0;
+        if ((uint32_t)kst * (kBK / 32) + ldb_chunk[n] >= kblocks || past_end) vo = kOOB;
+      }
       const int ix = kSubA * C::kLoadsA + n;
       if (part == 2 || (ix < kPart0) == (part == 0))
-        load16_to_lds(rw, buf + kSubA * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo);
+        load16_to_lds(rw, buf + kSubA * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo, so);
     }
   };
 
