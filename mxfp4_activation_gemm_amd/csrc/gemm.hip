@@ -150,7 +150,12 @@ struct TileCfg {
   static constexpr int kScaleBytes = F::kScalesA * kScaleBytesA + F::kScalesB * kBN * kScaleRowBytes;
   static constexpr int kLdsBytes = kRing * kStageBytes + kScaleBytes;
   static constexpr int kLoadsA = kBM / 16 / kWaves;    // 16-row DMA instructions per wave per sub-tile of X / R
-  static constexpr int kLoadsB = kBN / 16 / kWaves;    // for W
+  // for W; when the 16-row groups do not divide evenly among the waves,
+  // load n of wave w takes group (w + kWaves n) mod (kBN / 16), so a few
+  // groups are fetched twice (identical bytes to the same place)
+  static constexpr int kGroupsB = kBN / 16;
+  static constexpr bool kWrapB = kGroupsB % kWaves != 0;
+  static constexpr int kLoadsB = (kGroupsB + kWaves - 1) / kWaves;
   static_assert(kTM >= 1 && kTN >= 1 && kLoadsA >= 1 && kLoadsB >= 1, "tile shape");
   static_assert(!F::kM16 || (kT16M % 2 == 0 && kT16N % 2 == 0), "16 x 16 tiles come in halves");
   static_assert(kLdsBytes * kOcc <= 160 * 1024, "LDS budget per CU");
@@ -459,9 +464,13 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     lda_row[n] = kBM / kWaves * wave + 16 * n + (lane >> 2);
     lda_chunk[n] = (lane & 3) ^ swz(lda_row[n]);
   }
+  // first row of the 16-row group of W that load n of this wave fetches
+  auto ldb_group_row = [&](int n) __attribute__((always_inline)) -> uint32_t {
+    return C::kWrapB ? 16 * ((wave + kWaves * n) % C::kGroupsB) : kBN / kWaves * wave + 16 * n;
+  };
 #pragma unroll
   for (int n = 0; n < C::kLoadsB; ++n) {
-    const uint32_t row = kBN / kWaves * wave + 16 * n + (lane >> 2);
+    const uint32_t row = ldb_group_row(n) + (lane >> 2);
     ldb_chunk[n] = (lane & 3) ^ swz(row);
     ldb_voff[n] = row * kbytes + 16 * ldb_chunk[n];
   }
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       }
       const int ix = kSubA * C::kLoadsA + n;
       if (part == 2 || (ix < kPart0) == (part == 0))
-        load16_to_lds(rw, buf + kSubA * kTileBytesA + (kBN / kWaves * wave + 16 * n) * kRowBytes, vo, so);
+        load16_to_lds(rw, buf + kSubA * kTileBytesA + ldb_group_row(n) * kRowBytes, vo, so);
     }
   };
 
@@ -1114,6 +1123,28 @@ hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) 
   p.tiles_m = (p.M + p.gm - 1) / p.gm;
   p.tiles_n = (p.N + p.gn - 1) / p.gn;
   const int tiles = p.tiles_m * p.tiles_n;
+  if constexpr (F::kBf16 && !F::kOutT) {
+    // The bf16 product dY Wd: when 256 x 320 tiles (8 waves of 64 x 160)
+    // cover Y in whole rounds and 256 x 256 tiles would leave a partial
+    // one, the wide tiles run alone (dX of a layer with K = 5120: 16 x 16
+    // tiles per 4096 rows). They also do a quarter more MFMA work per stage
+    // and barrier.
+    using Wide = TileCfg<256, 320, 8, 1, F>;
+    const int wm = p.M / Wide::kBM, wn = p.N / Wide::kBN;
+    if (fast && p.vec_out && p.M % Wide::kBM == 0 && p.N % Wide::kBN == 0 && (int64_t)wm * wn % cus == 0 &&
+        tiles % cus != 0) {
+      p.gm = Wide::kBM;
+      p.gn = Wide::kBN;
+      p.tiles_m = wm;
+      p.tiles_n = wn;
+      p.first = 0;
+      p.grid = wm * wn;
+      p.pieces = 1;
+      const bool stream_tiles = p.grid > cus;
+      p.wg = stream_tiles ? cus : p.grid;
+      return launch_tiles<Wide, F, kOutBf16, true>(p, fast, stream_tiles, stream);
+    }
+  }
   const int rounds = tiles / cus, rest = tiles % cus;
   enum { kTailBig = 1, kTailQuad = 2, kTailHalf = 3 };
   int tail = kTailBig;

@@ -134,6 +134,26 @@ def test_full_size_sampled_and_adjoint():
     assert abs(a - b) <= 1e-4 * scale
 
 
+@pytest.mark.parametrize("M", [4096, 8192])
+def test_wide_tiles_every_output(M):
+    """dX outputs [M, 5120] that 256 x 320 tiles cover in whole rounds on 256
+    CUs (256 tiles: one per CU; 512: two streamed per CU) while 256 x 256
+    tiles would leave a partial round, the planner's case for the wide tiles
+    (as in dX of the 4096 x 5120 x 13824 layer): every output against the
+    oracle, with a short contraction N (a multiple of 128, which the wide
+    tiles need: the contraction in whole 512-element groups of the GEMM's
+    E2M1-sized K units)."""
+    N, K = 128, 5120
+    rng = np.random.default_rng(M + 13)
+    _, wb, dyb = make(rng, M, N, K)
+    log(f"[backward] wide-tile dX M={M} N={N} K={K}")
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    dx = rfq.backward_dx(dev_bf16(dyb), wq, sw, out_dtype=torch.bfloat16)
+    owq, osw = oracle.quantize_mxfp4(oracle.bf16_bits_to_f64(wb))
+    ref, s = oracle.backward_dx(oracle.bf16_bits_to_f64(dyb), owq, osw)
+    check_grad(g_host(dx), ref, s, N, torch.bfloat16, f"wide dX {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("which,M,N,K", [("dx", 4096, 128, 8192), ("dw", 128, 8192, 4096)])
 def test_streamed_tiles_every_output(which, M, N, K):
     """Output shapes of two whole rounds of 256 x 256 tiles on 256 CUs, so
