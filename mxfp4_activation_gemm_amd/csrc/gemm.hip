@@ -28,7 +28,9 @@
 // round's tiles are split, in a second launch, into upper and lower halves
 // (128 x 256 on 8 waves of 32 x 128, one workgroup per CU) or, for the
 // formats whose main tile is already 128 rows, into quadrants (4 waves,
-// two workgroups per CU).
+// two workgroups per CU). The bf16 product of the backward pass's dX also
+// has 256 x 320 tiles (8 waves of 64 x 160), used alone when they cover Y
+// in whole rounds and 256 x 256 tiles would not.
 //
 // Data movement:
 //  * Code tiles (QX, QR, W; 256 rows x 64 B each per stage) go global ->
