@@ -55,7 +55,7 @@ def test_tiny_config_every_output_fp32():
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 520, 416), (1, 1, 32), (33, 65, 96), (257, 255, 128), (70, 300, 4128),
-                                   (512, 512, 1024)])
+                                   (512, 512, 1024), (300, 520, 1024), (257, 1000, 512)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_ragged_shapes_every_output(M, N, K, out_dtype):
     rng = np.random.default_rng(M * 7 + N * 13 + K)
