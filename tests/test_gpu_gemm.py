@@ -8,8 +8,8 @@ import torch
 import mxfp4_activation_gemm_amd as rfq
 import oracle
 import workloads
-from gpu_helpers import (assert_bytes_equal, check_y, dev_bf16, dev_u8, host, host_bf16_as_f64, log, oracle_mx,
-                         oracle_rfq)
+from gpu_helpers import (REL_TOL, assert_bytes_equal, check_y, dev_bf16, dev_u8, host, host_bf16_as_f64, log,
+                         oracle_mx, oracle_rfq)
 
 pytestmark = pytest.mark.gpu
 
@@ -139,6 +139,31 @@ def test_nan_block_gives_nan_outputs_only_in_its_row():
     assert np.isnan(y[5]).all() and np.isnan(y[9]).all()
     ok_rows = [r for r in range(M) if r not in (5, 9)]
     assert np.isfinite(y[ok_rows]).all()
+
+
+def test_residual_term_is_the_difference_of_rfq_and_w4a4():
+    """End to end: Y_rfq - Y_w4a4, from two GPU GEMM calls on the same codes
+    (with and without the residual term), equals deq(Q(R)) deq(W)^T, the
+    residual path's contribution, within the two calls' accumulation bounds."""
+    rng = np.random.default_rng(321)
+    M, N, K = 200, 300, 1024
+    xb = heavy(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log("[gemm] residual term = RFQ - W4A4")
+    x = dev_bf16(xb)
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    qx, sx, qr, sr = rfq.residual_quantize(x)
+    y = rfq.gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.float32)
+    y1 = rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out_dtype=torch.float32)
+    diff = y_host(y) - y_host(y1)
+    oqx, osx, oqr, osr = oracle.residual_quantize(oracle.bf16_bits_to_f64(xb))
+    owq, osw = oracle.quantize_mxfp4(oracle.bf16_bits_to_f64(wb))
+    ref = oracle.dequantize(oqr, osr) @ oracle.dequantize(owq, osw).T
+    _, s = oracle.gemm_w4a4(oqx, osx, oqr, osr, owq, osw)
+    _, s1 = oracle.gemm_w4a4(oqx, osx, None, None, owq, osw)
+    err = np.abs(diff - ref)
+    assert (err <= REL_TOL * (s + s1) + 2.0 ** -125).all(), f"max err / S = {float(np.max(err / s)):.3e}"
+    assert np.abs(ref).max() > 0
 
 
 def test_linear_equals_quantize_then_gemm_bitwise_and_is_deterministic():
