@@ -141,6 +141,24 @@ def test_nan_block_gives_nan_outputs_only_in_its_row():
     assert np.isfinite(y[ok_rows]).all()
 
 
+def test_maximum_k_every_output():
+    """K at the ABI's limit, 2^22 (32768 stages, 131072 scale blocks per row):
+    every output of a 4 x 8 RFQ layer against the oracle. The fp32
+    accumulator takes 2K/128 step sums here, so the bound is the worst case
+    (2K/128 + 1) 2^-24 S of that many roundings rather than 1e-5 S."""
+    M, N, K = 4, 8, 1 << 22
+    rng = np.random.default_rng(99)
+    xb = heavy(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[gemm] maximum K = {K}")
+    y = rfq.linear(dev_bf16(xb), *rfq.quantize_mxfp4(dev_bf16(wb)), out_dtype=torch.float32)
+    y_ref, s_ref = oracle_y(xb, wb)
+    err = np.abs(y_host(y) - y_ref)
+    tol = (2 * K // 128 + 1) * 2.0 ** -24 * s_ref + 2.0 ** -126
+    assert (err <= tol).all(), f"max err / S = {float(np.max(err / s_ref)):.3e}"
+    log(f"   max |dY|/S = {float(np.max(err / s_ref)):.2e}")
+
+
 def test_residual_term_is_the_difference_of_rfq_and_w4a4():
     """End to end: Y_rfq - Y_w4a4, from two GPU GEMM calls on the same codes
     (with and without the residual term), equals deq(Q(R)) deq(W)^T, the
