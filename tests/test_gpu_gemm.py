@@ -151,7 +151,11 @@ def test_maximum_k_every_output():
     xb = heavy(rng, M, K)
     wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
     log(f"[gemm] maximum K = {K}")
-    y = rfq.linear(dev_bf16(xb), *rfq.quantize_mxfp4(dev_bf16(wb)), out_dtype=torch.float32)
+    x = dev_bf16(xb)
+    y = rfq.linear(x, *rfq.quantize_mxfp4(dev_bf16(wb)), out_dtype=torch.float32)
+    # the quantize pass at this K too: codes and scales byte-equal
+    for got, want, what in zip(rfq.residual_quantize(x), oracle_rfq(xb), ("QX", "SX", "QR", "SR")):
+        assert_bytes_equal(host(got), want, f"max-K {what}")
     y_ref, s_ref = oracle_y(xb, wb)
     err = np.abs(y_host(y) - y_ref)
     tol = (2 * K // 128 + 1) * 2.0 ** -24 * s_ref + 2.0 ** -126
