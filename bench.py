@@ -40,12 +40,20 @@ QUANT_R8_BYTES_PER_ELEM = 2 + (0.5 + 1.0 / 32) + (1 + 1.0 / 32)   # bf16 in, Q4(
 CPU_GEMM_ROWS = 4096                                  # rows of X in the oracle GEMM sample
 
 
+def progress(msg):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="wan22_ffn")
+    ap.add_argument("--ramp-seconds", type=float, default=1.0,
+                    help="untimed steps run for this long before the warmup steps, so that the GPU has left its "
+                         "idle clock state (reported as clock_ramp in the JSON)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-hbm-quantize", action="store_true",
                     help="skip the extra quantize measurement on the long-sequence layer")
@@ -176,7 +184,8 @@ def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=No
     `e4m3` (MXFP8 activation codes) it times the E2M1 x E4M3 instruction of
     the W4A8 GEMM instead (rfq_probe_mfma_ceiling_e4m3: weight codes first,
     E4M3 codes second)."""
-    lib = rfq.library()
+    import bench_probe
+    lib = bench_probe.load()
     props = torch.cuda.get_device_properties(0)
     wgs = props.multi_processor_count
     if e4m3 is None:
@@ -190,8 +199,8 @@ def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=No
         fn = lib.rfq_probe_mfma_ceiling_e4m3
     stamps = torch.zeros(2 * wgs, dtype=torch.int64, device=qx.device)
     sink = torch.empty(512 * wgs, dtype=torch.float32, device=qx.device)
-    call = lambda: rfq._lib.check(fn(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), wgs, iters, stamps.data_ptr(),
-                                     sink.data_ptr(), sp))
+    call = lambda: bench_probe.check(fn(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), wgs, iters,
+                                        stamps.data_ptr(), sink.data_ptr(), sp))
     call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -276,6 +285,7 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
+    progress(f"generating {cfg.name} inputs")
     x = to_dev(workloads.x_bf16(cfg))
     w = to_dev(workloads.w_bf16(cfg))
     wq, sw = rfq.quantize_mxfp4(w)                 # setup: the weight is quantized once
@@ -306,6 +316,19 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    # Clock ramp: generating the inputs on the host leaves the GPU idle for
+    # several seconds, and a few warmup steps (~0.3 ms each) are not enough
+    # for it to leave its idle clock state; so untimed steps run for
+    # --ramp-seconds first, then the --warmup steps, then the timed steps.
+    progress("clock ramp, warmup and timed steps")
+    torch.cuda.synchronize()
+    ramp_steps, t_ramp = 0, time.perf_counter()
+    while time.perf_counter() - t_ramp < args.ramp_seconds:
+        for _ in range(50):
+            step()
+        ramp_steps += 50
+        torch.cuda.synchronize()
+    ramp_s = time.perf_counter() - t_ramp
     for _ in range(args.warmup):
         step()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -332,6 +355,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    progress("kernel timings")
     quant_ms = batch_ms(quantize, 100)
 
     # the same pass with its inputs and outputs rotated over 8 buffer sets
@@ -427,6 +451,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        "clock_ramp": {"untimed_steps": ramp_steps, "seconds": round(ramp_s, 3),
+                       "note": "untimed steps before the warmup steps, so that the GPU leaves its idle clock state "
+                               "after the host-side input generation"},
         "dtype": "fp4",
         "data": "synthetic",
         "config": {
@@ -448,6 +475,8 @@ def main():
             "median_launch_us": round(float(np.median(gemm_times)) * 1e3, 2),
             "iqr_launch_us": [round(float(np.percentile(gemm_times, 25)) * 1e3, 2),
                               round(float(np.percentile(gemm_times, 75)) * 1e3, 2)],
+            "first_launches_us": [round(float(t) * 1e3, 2) for t in gemm_times[:5]],
+            "last_launches_us": [round(float(t) * 1e3, 2) for t in gemm_times[-5:]],
             "measured_mfma_ceiling": dict(ceiling, frac_of_ceiling=round(gemm_tflops / ceiling["TFLOP_per_s"], 4)),
         },
         "kernels": {
@@ -523,6 +552,7 @@ def main():
         },
     }
     sweep = {}
+    progress("configuration sweep")
     if not args.no_sweep:
         sweep[cfg.name] = layer_timings(rfq, torch, cfg, x, wq, sw, batch_ms, 50)
     del qx, qr, sx, sr, y, x
@@ -602,6 +632,7 @@ def main():
         out["copy_calibration_bytes"] = a.numel()
 
     if not args.no_cpu_baseline:
+        progress("oracle timing on the host")
         out["cpu_baseline"] = cpu_baseline(cfg)
         if not args.no_sweep:
             out["cpu_baseline"]["per_config"] = oracle_config_timings()

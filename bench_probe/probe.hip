@@ -1,5 +1,6 @@
-// MFMA issue ceiling under the power limit (measurement probe, not part of
-// the RFQ layer): a loop of the GEMM's scaled MFMA on caller-supplied
+// MFMA issue ceiling under the power limit: a benchmark-only probe, built
+// into its own library (librfqprobe.so) beside bench.py and never linked
+// into librfq.so. It runs a loop of the GEMM's scaled MFMA on caller-supplied
 // operand bytes, with no memory traffic inside the loop, timed per workgroup
 // in shader-clock cycles (s_memtime) and in 100 MHz constant-clock ticks
 // (s_memrealtime), so that both the rate and the clock it ran at can be read
@@ -8,9 +9,11 @@
 // the 32 x 32 x 64 form of the MXFP8 activation variants (32 instructions
 // over 8 accumulators). Both do the same flops per iteration.
 
-#include "kernels.h"
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
-namespace rfq {
+#include "rfq_probe.h"
+
 namespace {
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -90,8 +93,16 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a
 
 }  // namespace
 
-hipError_t launch_mfma_ceiling(const uint8_t* a, size_t a_bytes, const uint8_t* b, size_t b_bytes, int b_fmt,
-                               int workgroups, int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
+namespace {
+
+int launch_probe(const uint8_t* a, size_t a_bytes, const uint8_t* b, size_t b_bytes, int b_fmt, int workgroups,
+                 int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
+  if (a == nullptr || b == nullptr || stamps == nullptr || sink == nullptr) return RFQ_PROBE_ERR_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(b) % 16) return RFQ_PROBE_ERR_ARGUMENT;
+  const size_t max_bytes = (size_t(1) << 32) * 16 - 16;
+  if (a_bytes < 16 || b_bytes < 16 || a_bytes % 16 || b_bytes % 16 || a_bytes > max_bytes || b_bytes > max_bytes)
+    return RFQ_PROBE_ERR_ARGUMENT;
+  if (workgroups <= 0 || workgroups > 65536 || iters <= 0) return RFQ_PROBE_ERR_ARGUMENT;
   const auto* ap = reinterpret_cast<const i32x4_t*>(a);
   const auto* bp = reinterpret_cast<const i32x4_t*>(b);
   if (b_fmt == 8)
@@ -100,7 +111,23 @@ hipError_t launch_mfma_ceiling(const uint8_t* a, size_t a_bytes, const uint8_t* 
   else
     hipLaunchKernelGGL(mfma_ceiling_kernel<4>, dim3(workgroups), dim3(kThreads), 0, stream, ap, (uint32_t)(a_bytes / 16),
                        bp, (uint32_t)(b_bytes / 16), iters, stamps, sink);
-  return hipGetLastError();
+  return hipGetLastError() == hipSuccess ? RFQ_PROBE_OK : RFQ_PROBE_ERR_HIP;
 }
 
-}  // namespace rfq
+}  // namespace
+
+extern "C" {
+
+int rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
+                           int workgroups, int iters, uint64_t* stamps, float* sink, void* stream) {
+  return launch_probe(a_codes, a_bytes, b_codes, b_bytes, 4, workgroups, iters, stamps, sink,
+                      static_cast<hipStream_t>(stream));
+}
+
+int rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
+                                int workgroups, int iters, uint64_t* stamps, float* sink, void* stream) {
+  return launch_probe(a_codes, a_bytes, b_codes, b_bytes, 8, workgroups, iters, stamps, sink,
+                      static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

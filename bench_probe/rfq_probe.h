@@ -1,5 +1,7 @@
 /*
- * rfq_probe.h - measurement probe of librfq (not part of the RFQ layer).
+ * rfq_probe.h - benchmark-only measurement probe, built into its own
+ * library (bench_probe/librfqprobe.so) and loaded only by bench.py; it is not
+ * part of librfq.so or of the RFQ layer.
  *
  * The FP4 GEMM on MI355X is limited by the chip's power budget before the
  * MFMA issue rate: with real operand data the shader clock drops well below
@@ -16,11 +18,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "rfq.h"
 
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Return codes of the probe calls. */
+enum { RFQ_PROBE_OK = 0, RFQ_PROBE_ERR_ARGUMENT = 1, RFQ_PROBE_ERR_HIP = 2 };
 
 /*
  * rfq_probe_mfma_ceiling - launch `workgroups` workgroups of 512 threads
@@ -39,10 +43,13 @@ extern "C" {
  *     written so that the loop is not optimised away.
  * Flops per call: 2 * 32 * 32 * 64 * 32 * 8 * iters * workgroups (8 waves of
  * 64 MFMAs of 2 * 16 * 16 * 128 flops per iteration). Asynchronous on
- * `stream`; errors as in rfq.h.
+ * `stream` (a hipStream_t; NULL is the null stream). Returns
+ * RFQ_PROBE_ERR_ARGUMENT for a NULL or misaligned buffer, a size that is not
+ * a multiple of 16 in [16, 2^36), workgroups outside [1, 65536] or iters <= 0
+ * (nothing launched), RFQ_PROBE_ERR_HIP if the launch failed.
  */
-rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
-                                    int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream);
+int rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
+                           int workgroups, int iters, uint64_t* stamps, float* sink, void* stream);
 
 /*
  * rfq_probe_mfma_ceiling_e4m3 - the same measurement for the instruction of
@@ -53,9 +60,8 @@ rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, cons
  * size; all else as rfq_probe_mfma_ceiling, including the flop count per
  * call.
  */
-rfq_status_t rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes,
-                                         size_t b_bytes, int workgroups, int iters, uint64_t* stamps, float* sink,
-                                         rfq_stream_t stream);
+int rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
+                                int workgroups, int iters, uint64_t* stamps, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RFQ_ABI_VERSION 4
+#define RFQ_ABI_VERSION 5
 
 typedef enum rfq_status {
   RFQ_OK = 0,

@@ -51,38 +51,119 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _x_args(x):
-    """(rows, K, ldx, dtype code) of a 2-D bf16 or fp32 CUDA tensor with unit stride along K."""
-    if x.dtype not in (torch.bfloat16, torch.float32) or x.dim() != 2 or not x.is_cuda:
-        raise ValueError("x must be a 2-D bfloat16 or float32 CUDA tensor")
-    if x.stride(1) != 1:
-        raise ValueError("x must have unit stride along K")
-    return x.shape[0], x.shape[1], x.stride(0), (DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_FP32)
+# Shape rules. The C ABI receives raw device pointers, so this binding is the
+# only layer that can see a tensor's shape, dtype, strides and device: every
+# operand is checked here, before any call into the library, and a mismatch
+# raises ValueError with nothing launched and no output written. The rules
+# below look only at tensor metadata (no device access), so they also run on
+# CPU tensors.
+
+def _fail(what, msg):
+    raise ValueError(f"{what}: {msg}")
 
 
-def _y_dtype(out_dtype):
-    if out_dtype == torch.float32:
-        return DTYPE_FP32
-    if out_dtype == torch.bfloat16:
-        return DTYPE_BF16
-    raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+def _check_matrix(t, what, dtypes, rows=None, cols=None, dense=True):
+    """A 2-D tensor of one of `dtypes`, [rows, cols] where given, unit stride
+    along its last dimension, and (dense) fully contiguous."""
+    if not isinstance(t, torch.Tensor):
+        _fail(what, "must be a torch.Tensor")
+    if t.dim() != 2:
+        _fail(what, f"must be 2-D, got shape {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        _fail(what, f"dtype {t.dtype} not in {[str(d) for d in dtypes]}")
+    if rows is not None and t.shape[0] != rows:
+        _fail(what, f"has {t.shape[0]} rows, expected {rows}")
+    if cols is not None and t.shape[1] != cols:
+        _fail(what, f"has {t.shape[1]} columns, expected {cols}")
+    if t.numel() and t.stride(1) != 1:
+        _fail(what, f"must have unit stride along its last dimension, got strides {t.stride()}")
+    if dense and t.numel() and not t.is_contiguous():
+        _fail(what, "must be contiguous")
+
+
+_U8 = (torch.uint8,)
+_XTYPES = (torch.bfloat16, torch.float32)
+_YTYPES = (torch.float32, torch.bfloat16)
+
+
+def check_codes(codes, scales, rows, K, what, element_bytes=0.5):
+    """MX codes [rows, K * element_bytes] (0.5: MXFP4 nibbles, 1: MXFP8 bytes)
+    and scales [rows, K / 32], both contiguous uint8."""
+    if K % 32:
+        _fail(what, f"K = {K} is not a multiple of 32")
+    _check_matrix(codes, f"{what} codes", _U8, rows, int(K * element_bytes))
+    _check_matrix(scales, f"{what} scales", _U8, rows, K // 32)
+
+
+def check_x(x, what="x"):
+    """X [M, K] bf16 or fp32 with unit stride along K (any row stride); returns (M, K)."""
+    _check_matrix(x, what, _XTYPES, dense=False)
+    return x.shape[0], x.shape[1]
+
+
+def check_out(out, rows, cols, what="out"):
+    """An output [rows, cols] fp32 or bf16 with unit column stride and a row
+    stride of at least cols (rows may be strided, as the ABI's ldy allows)."""
+    _check_matrix(out, what, _YTYPES, rows, cols, dense=False)
+    if rows > 1 and cols and out.stride(0) < cols:
+        _fail(what, f"row stride {out.stride(0)} is below its {cols} columns")
+
+
+def check_workspace(ws, need, what="workspace"):
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        _fail(what, "must be a contiguous uint8 tensor")
+    if ws.numel() < need:
+        _fail(what, f"holds {ws.numel()} bytes, needs {need}")
+
+
+def check_device(device, **tensors):
+    """Every tensor on `device`, a CUDA device."""
+    if device.type != "cuda":
+        raise ValueError(f"operands must be CUDA tensors, got device {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            _fail(name, f"is on {t.device}, expected {device}")
+
+
+def _given_out(out, rows, cols):
+    if out is not None:
+        check_out(out, rows, cols)
+
+
+def _new_out(out, rows, cols, out_dtype, device):
+    if out is None:
+        if out_dtype not in _YTYPES:
+            raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+        out = torch.empty((rows, cols), dtype=out_dtype, device=device)
+    check_out(out, rows, cols)
+    return out
+
+
+def _x_code(x):
+    return DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_FP32
+
+
+def _y_code(y):
+    return DTYPE_FP32 if y.dtype == torch.float32 else DTYPE_BF16
 
 
 def _quantize(fn, x, bytes_per_element=0.5):
-    rows, K, ldx, dt = _x_args(x)
+    rows, K = check_x(x)
+    check_device(x.device, x=x)
     codes = torch.empty((rows, int(K * bytes_per_element)), dtype=torch.uint8, device=x.device)
     scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
-    check(fn(_ptr(x), dt, rows, K, ldx, _ptr(codes), _ptr(scales), _stream()))
+    check(fn(_ptr(x), _x_code(x), rows, K, x.stride(0), _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
 
 
 def _residual(fn, x, r_bytes_per_element=0.5):
-    M, K, ldx, dt = _x_args(x)
+    M, K = check_x(x)
+    check_device(x.device, x=x)
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     qr = torch.empty((M, int(K * r_bytes_per_element)), dtype=torch.uint8, device=x.device)
     sx = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     sr = torch.empty_like(sx)
-    check(fn(_ptr(x), dt, M, K, ldx, _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), _stream()))
+    check(fn(_ptr(x), _x_code(x), M, K, x.stride(0), _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), _stream()))
     return qx, sx, qr, sr
 
 
@@ -106,28 +187,31 @@ def rotate_quantize_weight(w):
     return _quantize(load().rfq_rotate_quantize_weight, w)
 
 
-def _codes_ok(*ts):
-    for t in ts:
-        if t is not None and (t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda):
-            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
-
-
-def _out(y, M, N, out_dtype, device):
-    y = y if y is not None else torch.empty((M, N), dtype=out_dtype, device=device)
-    if y.stride(1) != 1:
-        raise ValueError("out must have unit stride along N")
-    return y
+def gemm_shapes(qx, sx, qr, sr, wq, sw, x_bytes=0.5, r_bytes=0.5):
+    """(M, N, K) of a block-scaled GEMM's operands after checking them against
+    each other: activation codes [M, K * x_bytes], residual codes [M, K * r_bytes]
+    (or qr = sr = None), weight codes [N, K/2], every scale tensor [rows, K/32]."""
+    _check_matrix(qx, "QX codes", _U8)
+    M, K = qx.shape[0], int(round(qx.shape[1] / x_bytes))
+    _check_matrix(wq, "W codes", _U8)
+    N = wq.shape[0]
+    check_codes(qx, sx, M, K, "QX", x_bytes)
+    if (qr is None) != (sr is None):
+        raise ValueError("QR codes and scales must be given together")
+    if qr is not None:
+        check_codes(qr, sr, M, K, "QR", r_bytes)
+    check_codes(wq, sw, N, K, "W")
+    return M, N, K
 
 
 def gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.bfloat16, out=None):
     """Y = deq(QX) deq(W)^T + deq(QR) deq(W)^T (qr = sr = None: plain W4A4)."""
-    M, N, K = qx.shape[0], wq.shape[0], qx.shape[1] * 2
-    _codes_ok(qx, sx, qr, sr, wq, sw)
-    if wq.shape[1] * 2 != K:
-        raise ValueError("QX and W disagree on K")
-    y = _out(out, M, N, out_dtype, qx.device)
+    M, N, K = gemm_shapes(qx, sx, qr, sr, wq, sw)
+    _given_out(out, M, N)
+    check_device(qx.device, sx=sx, qr=qr, sr=sr, wq=wq, sw=sw, out=out)
+    y = _new_out(out, M, N, out_dtype, qx.device)
     check(load().rfq_gemm_w4a4(_ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), _ptr(wq), _ptr(sw), M, N, K, _ptr(y),
-                               _y_dtype(y.dtype), y.stride(0), _stream()))
+                               _y_code(y), y.stride(0), _stream()))
     return y
 
 
@@ -143,61 +227,81 @@ def residual_quantize_mxfp8(x):
 
 def gemm_w4a8(qx8, sx, wq, sw, out_dtype=torch.bfloat16, out=None):
     """Y = deq(QX8) deq(W)^T for MXFP8 activation codes and the MXFP4 weight."""
-    M, N, K = qx8.shape[0], wq.shape[0], qx8.shape[1]
-    _codes_ok(qx8, sx, wq, sw)
-    if wq.shape[1] * 2 != K:
-        raise ValueError("QX and W disagree on K")
-    y = _out(out, M, N, out_dtype, qx8.device)
-    check(load().rfq_gemm_w4a8(_ptr(qx8), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _y_dtype(y.dtype),
+    M, N, K = gemm_shapes(qx8, sx, None, None, wq, sw, x_bytes=1)
+    _given_out(out, M, N)
+    check_device(qx8.device, sx=sx, wq=wq, sw=sw, out=out)
+    y = _new_out(out, M, N, out_dtype, qx8.device)
+    check(load().rfq_gemm_w4a8(_ptr(qx8), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _y_code(y),
                                y.stride(0), _stream()))
     return y
 
 
 def gemm_w4a4_mxfp8_residual(qx, sx, qr8, sr, wq, sw, out_dtype=torch.bfloat16, out=None):
     """Y = deq(QX) deq(W)^T + deq(QR8) deq(W)^T, QX MXFP4 and QR8 MXFP8."""
-    M, N, K = qx.shape[0], wq.shape[0], qx.shape[1] * 2
-    _codes_ok(qx, sx, qr8, sr, wq, sw)
-    if wq.shape[1] * 2 != K or qr8.shape[1] != K:
-        raise ValueError("operands disagree on K")
-    y = _out(out, M, N, out_dtype, qx.device)
+    if qr8 is None or sr is None:
+        raise ValueError("the MXFP8 residual term (qr8, sr) is required")
+    M, N, K = gemm_shapes(qx, sx, qr8, sr, wq, sw, r_bytes=1)
+    _given_out(out, M, N)
+    check_device(qx.device, sx=sx, qr8=qr8, sr=sr, wq=wq, sw=sw, out=out)
+    y = _new_out(out, M, N, out_dtype, qx.device)
     check(load().rfq_gemm_w4a4_mxfp8_residual(_ptr(qx), _ptr(sx), _ptr(qr8), _ptr(sr), _ptr(wq), _ptr(sw), M, N, K,
-                                              _ptr(y), _y_dtype(y.dtype), y.stride(0), _stream()))
+                                              _ptr(y), _y_code(y), y.stride(0), _stream()))
     return y
 
 
-def _dy_args(dy):
-    if dy.dtype != torch.bfloat16 or dy.dim() != 2 or not dy.is_cuda or dy.stride(1) != 1:
-        raise ValueError("dy must be a 2-D bfloat16 CUDA tensor with unit stride along N")
-    return dy.shape[0], dy.shape[1], dy.stride(0)
+def check_dy(dy, dense):
+    """dY [M, N] bf16 with unit stride along N; `dense` also requires rows
+    back to back (row stride N), as rfq_backward_dx does. Returns (M, N)."""
+    _check_matrix(dy, "dy", (torch.bfloat16,), dense=False)
+    M, N = dy.shape
+    if dense and M > 1 and dy.stride(0) != N:
+        _fail("dy", f"must be dense (row stride {N}), got row stride {dy.stride(0)}")
+    return M, N
 
 
 def backward_dx(dy, wq, sw, out_dtype=torch.float32, out=None, workspace=None):
     """Straight-through dX = dY deq(Wq) for bf16 dY [M, N] (dense) and the
-    weight's MXFP4 codes/scales; returns dX [M, K]."""
-    M, N, lddy = _dy_args(dy)
-    _codes_ok(wq, sw)
+    weight's MXFP4 codes/scales [N, K/2], [N, K/32]; returns dX [M, K]."""
+    M, N = check_dy(dy, dense=True)
+    _check_matrix(wq, "W codes", _U8, rows=N)
     K = wq.shape[1] * 2
-    dx = _out(out, M, K, out_dtype, dy.device)
+    check_codes(wq, sw, N, K, "W")
+    _given_out(out, M, K)
+    if workspace is not None:
+        check_workspace(workspace, 0)
+    check_device(dy.device, wq=wq, sw=sw, out=out, workspace=workspace)
     need = int(load().rfq_backward_dx_workspace_size(N, K))
+    if workspace is not None:
+        check_workspace(workspace, need)
+    dx = _new_out(out, M, K, out_dtype, dy.device)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dy.device)
-    check(load().rfq_backward_dx(_ptr(dy), DTYPE_BF16, M, N, lddy, _ptr(wq), _ptr(sw), K, _ptr(dx), _y_dtype(dx.dtype),
-                                 dx.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    check(load().rfq_backward_dx(_ptr(dy), DTYPE_BF16, M, N, dy.stride(0), _ptr(wq), _ptr(sw), K, _ptr(dx),
+                                 _y_code(dx), dx.stride(0), _ptr(workspace), workspace.numel(), _stream()))
     return dx
 
 
 def backward_dw(dy, qx, sx, qr, sr, out_dtype=torch.float32, out=None, workspace=None):
     """Straight-through dW = dY^T (deq Q(X) + deq Q(R)) for bf16 dY [M, N] and
-    the forward's RFQ encoding of X; returns dW [N, K]."""
-    M, N, lddy = _dy_args(dy)
-    _codes_ok(qx, sx, qr, sr)
+    the forward's RFQ encoding of X ([M, K/2] codes, [M, K/32] scales each);
+    returns dW [N, K]."""
+    M, N = check_dy(dy, dense=False)
+    _check_matrix(qx, "QX codes", _U8, rows=M)
     K = qx.shape[1] * 2
-    dw = _out(out, N, K, out_dtype, dy.device)
+    check_codes(qx, sx, M, K, "QX")
+    check_codes(qr, sr, M, K, "QR")
+    _given_out(out, N, K)
+    if workspace is not None:
+        check_workspace(workspace, 0)
+    check_device(dy.device, qx=qx, sx=sx, qr=qr, sr=sr, out=out, workspace=workspace)
     need = int(load().rfq_backward_dw_workspace_size(M, N, K))
+    if workspace is not None:
+        check_workspace(workspace, need)
+    dw = _new_out(out, N, K, out_dtype, dy.device)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dy.device)
-    check(load().rfq_backward_dw(_ptr(dy), DTYPE_BF16, M, N, lddy, _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), K, _ptr(dw),
-                                 _y_dtype(dw.dtype), dw.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    check(load().rfq_backward_dw(_ptr(dy), DTYPE_BF16, M, N, dy.stride(0), _ptr(qx), _ptr(sx), _ptr(qr), _ptr(sr), K,
+                                 _ptr(dw), _y_code(dw), dw.stride(0), _ptr(workspace), workspace.numel(), _stream()))
     return dw
 
 
@@ -205,14 +309,28 @@ def linear_workspace_size(M, K):
     return int(load().rfq_linear_workspace_size(M, K))
 
 
+def linear_shapes(x, wq, sw):
+    """(M, N, K) of the layer after checking X [M, K] against the weight's
+    codes [N, K/2] and scales [N, K/32]."""
+    M, K = check_x(x)
+    _check_matrix(wq, "W codes", _U8)
+    check_codes(wq, sw, wq.shape[0], K, "W")
+    return M, wq.shape[0], K
+
+
 def linear(x, wq, sw, out_dtype=torch.bfloat16, out=None, workspace=None):
-    """Whole RFQ W4A4 linear layer on bf16 X [M, K] and an MXFP4 weight."""
-    M, K, ldx, dt = _x_args(x)
-    N = wq.shape[0]
-    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    """Whole RFQ W4A4 linear layer on bf16 or fp32 X [M, K] and an MXFP4 weight."""
+    M, N, K = linear_shapes(x, wq, sw)
+    _given_out(out, M, N)
+    if workspace is not None:
+        check_workspace(workspace, 0)
+    check_device(x.device, wq=wq, sw=sw, out=out, workspace=workspace)
     need = linear_workspace_size(M, K)
+    if workspace is not None:
+        check_workspace(workspace, need)
+    y = _new_out(out, M, N, out_dtype, x.device)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    check(load().rfq_linear(_ptr(x), dt, M, K, ldx, _ptr(wq), _ptr(sw), N, _ptr(y), _y_dtype(y.dtype),
+    check(load().rfq_linear(_ptr(x), _x_code(x), M, K, x.stride(0), _ptr(wq), _ptr(sw), N, _ptr(y), _y_code(y),
                             y.stride(0), _ptr(workspace), workspace.numel(), _stream()))
     return y

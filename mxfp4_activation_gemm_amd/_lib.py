@@ -34,8 +34,6 @@ SIGNATURES = {
     "rfq_status_string": (ctypes.c_char_p, [_i]),
     "rfq_last_error_detail": (ctypes.c_char_p, []),
     "rfq_abi_version": (_i, []),
-    "rfq_probe_mfma_ceiling": (_i, [_p, _sz, _p, _sz, _i, _i, _p, _p, _p]),
-    "rfq_probe_mfma_ceiling_e4m3": (_i, [_p, _sz, _p, _sz, _i, _i, _p, _p, _p]),
     "rfq_quantize_mxfp8": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p]),
     "rfq_residual_quantize_mxfp8": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "rfq_gemm_w4a8": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _i64, _p]),

@@ -9,7 +9,6 @@
 
 #include "kernels.h"
 #include "rfq.h"
-#include "rfq_probe.h"
 
 namespace {
 
@@ -150,6 +149,39 @@ rfq_status_t gemm_common(int x_fmt, int r_fmt, const uint8_t* qx_codes, const ui
                                    y_dtype == RFQ_DTYPE_BF16, ldy, static_cast<hipStream_t>(stream)));
 }
 
+// Checks shared by the two linear entry points (everything but the workspace).
+rfq_status_t check_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* w_codes,
+                          const uint8_t* w_scales, int64_t N, const void* y, int y_dtype, int64_t ldy) {
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_rows_k(N, K, "N"));
+  RFQ_TRY(check_mn(M, N));
+  RFQ_TRY(check_dtype(x_dtype));
+  if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
+  if (M == 0 || N == 0) return RFQ_OK;
+  RFQ_TRY(check_x(x, x_dtype, K, ldx));
+  RFQ_TRY(check_codes(w_codes, w_scales, "W"));
+  RFQ_TRY(check_y(y, y_dtype, N, ldy));
+  return RFQ_OK;
+}
+
+// The layer's two launches with Q(X) | SX | Q(R) | SR staged at `ws` (the
+// regions of rfq_linear_workspace_size); arguments already checked.
+rfq_status_t linear_launch(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* w_codes,
+                           const uint8_t* w_scales, int64_t N, void* y, int y_dtype, int64_t ldy, uint8_t* ws,
+                           rfq_stream_t stream) {
+  const size_t codes = round256((size_t)(M * (K / 2))), scales = round256((size_t)(M * (K / 32)));
+  uint8_t* qx = ws;
+  uint8_t* sx = qx + codes;
+  uint8_t* qr = sx + scales;
+  uint8_t* sr = qr + codes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, 0, 4, 4, M, K, ldx, qx, sx, qr, sr, s);
+  if (e != hipSuccess) return launched(e);
+  return launched(rfq::launch_gemm(4, 4, qx, sx, qr, sr, w_codes, w_scales, M, N, K, y, y_dtype == RFQ_DTYPE_BF16, ldy,
+                                   s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -224,33 +256,15 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                         const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                         void* y, int y_dtype, int64_t ldy,
                         void* workspace, size_t workspace_bytes, rfq_stream_t stream) {
-  RFQ_TRY(check_rows_k(M, K, "M"));
-  RFQ_TRY(check_rows_k(N, K, "N"));
-  RFQ_TRY(check_mn(M, N));
-  RFQ_TRY(check_dtype(x_dtype));
-  if (y_dtype != RFQ_DTYPE_FP32 && y_dtype != RFQ_DTYPE_BF16)
-    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "y_dtype %d: must be RFQ_DTYPE_FP32 or RFQ_DTYPE_BF16", y_dtype);
+  RFQ_TRY(check_linear(x, x_dtype, M, K, ldx, w_codes, w_scales, N, y, y_dtype, ldy));
   if (M == 0 || N == 0) return ok();
-  RFQ_TRY(check_x(x, x_dtype, K, ldx));
-  RFQ_TRY(check_codes(w_codes, w_scales, "W"));
-  RFQ_TRY(check_y(y, y_dtype, N, ldy));
   if (workspace == nullptr) return fail(RFQ_ERR_NULL_POINTER, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(RFQ_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   const size_t need = rfq_linear_workspace_size(M, K);
   if (workspace_bytes < need)
     return fail(RFQ_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes = %zu, need %zu", workspace_bytes, need);
-
-  const size_t codes = round256((size_t)(M * (K / 2))), scales = round256((size_t)(M * (K / 32)));
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* qx = ws;
-  uint8_t* sx = qx + codes;
-  uint8_t* qr = sx + scales;
-  uint8_t* sr = qr + codes;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = rfq::launch_quantize(x, x_dtype == RFQ_DTYPE_FP32, 0, 4, 4, M, K, ldx, qx, sx, qr, sr, s);
-  if (e != hipSuccess) return launched(e);
-  return launched(rfq::launch_gemm(4, 4, qx, sx, qr, sr, w_codes, w_scales, M, N, K, y, y_dtype == RFQ_DTYPE_BF16, ldy,
-                                   s));
+  return linear_launch(x, x_dtype, M, K, ldx, w_codes, w_scales, N, y, y_dtype, ldy,
+                       static_cast<uint8_t*>(workspace), stream);
 }
 
 size_t rfq_backward_dx_workspace_size(int64_t N, int64_t K) {
@@ -354,38 +368,5 @@ const char* rfq_status_string(rfq_status_t status) {
 const char* rfq_last_error_detail(void) { return g_detail.c_str(); }
 
 int rfq_abi_version(void) { return RFQ_ABI_VERSION; }
-
-}  // extern "C"
-
-namespace {
-
-rfq_status_t probe_common(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes, int b_fmt,
-                          int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream) {
-  if (a_codes == nullptr || b_codes == nullptr || stamps == nullptr || sink == nullptr)
-    return fail(RFQ_ERR_NULL_POINTER, "probe buffers must not be NULL");
-  if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return fail(RFQ_ERR_MISALIGNED, "operands must be 16-byte aligned");
-  const size_t max_bytes = (size_t(1) << 32) * 16 - 16;
-  if (a_bytes < 16 || b_bytes < 16 || a_bytes % 16 || b_bytes % 16 || a_bytes > max_bytes || b_bytes > max_bytes)
-    return fail(RFQ_ERR_INVALID_SHAPE, "operand sizes must be multiples of 16 in [16, 2^36)");
-  if (workgroups <= 0 || workgroups > 65536 || iters <= 0)
-    return fail(RFQ_ERR_INVALID_SHAPE, "workgroups must be in [1, 65536] and iters positive");
-  return launched(rfq::launch_mfma_ceiling(a_codes, a_bytes, b_codes, b_bytes, b_fmt, workgroups, iters, stamps, sink,
-                                           static_cast<hipStream_t>(stream)));
-}
-
-}  // namespace
-
-extern "C" {
-
-rfq_status_t rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
-                                    int workgroups, int iters, uint64_t* stamps, float* sink, rfq_stream_t stream) {
-  return probe_common(a_codes, a_bytes, b_codes, b_bytes, 4, workgroups, iters, stamps, sink, stream);
-}
-
-rfq_status_t rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes,
-                                         size_t b_bytes, int workgroups, int iters, uint64_t* stamps, float* sink,
-                                         rfq_stream_t stream) {
-  return probe_common(a_codes, a_bytes, b_codes, b_bytes, 8, workgroups, iters, stamps, sink, stream);
-}
 
 }  // extern "C"

@@ -37,9 +37,4 @@ hipError_t launch_decode_transpose(const uint8_t* codes, const uint8_t* scales, 
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld_in, uint16_t* out,
                                  int64_t ld_out, hipStream_t stream);
 
-// Measurement probe: the scaled MFMA loop on caller-supplied operands (first
-// operand E2M1, second E2M1 or, b_fmt 8, E4M3).
-hipError_t launch_mfma_ceiling(const uint8_t* a, size_t a_bytes, const uint8_t* b, size_t b_bytes, int b_fmt,
-                               int workgroups, int iters, uint64_t* stamps, float* sink, hipStream_t stream);
-
 }  // namespace rfq

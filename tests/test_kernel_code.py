@@ -14,17 +14,20 @@ import subprocess
 
 import pytest
 
-CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "mxfp4_activation_gemm_amd", "csrc")
-INCLUDE = os.path.join(os.path.dirname(CSRC), "..", "include")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mxfp4_activation_gemm_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+PROBE = os.path.join(ROOT, "bench_probe")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not available")
-@pytest.mark.parametrize("source", ["gemm.hip", "quantize.hip", "backward.hip", "probe.hip"])
+@pytest.mark.parametrize("source", [os.path.join(CSRC, "gemm.hip"), os.path.join(CSRC, "quantize.hip"),
+                                    os.path.join(CSRC, "backward.hip"), os.path.join(PROBE, "probe.hip")])
 def test_kernels_make_no_calls_and_use_no_scratch(source, tmp_path):
-    out = tmp_path / (source + ".s")
+    out = tmp_path / (os.path.basename(source) + ".s")
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC, "-S", "--cuda-device-only", os.path.join(CSRC, source),
+           "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC, "-I", PROBE, "-S", "--cuda-device-only", source,
            "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
