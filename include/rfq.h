@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RFQ_ABI_VERSION 5
+#define RFQ_ABI_VERSION 6
 
 typedef enum rfq_status {
   RFQ_OK = 0,
@@ -267,6 +267,32 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                         const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                         void* y, int y_dtype, int64_t ldy,
                         void* workspace, size_t workspace_bytes, rfq_stream_t stream);
+
+/*
+ * rfq_linear_noalloc - rfq_linear for callers that cannot allocate memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same layer, arguments, layout and errors as rfq_linear, but
+ * with no workspace argument: Q(X) and Q(R) are staged in a device array that
+ * the library owns, rfq_linear_noalloc_max_workspace() bytes (64 MiB) on each
+ * GPU it runs on, held until the process ends. The call allocates nothing.
+ *   - A shape whose rfq_linear_workspace_size(M, K) exceeds that size is
+ *     rejected with RFQ_ERR_WORKSPACE_TOO_SMALL before anything is launched
+ *     (K = 5120 allows M up to 12 k rows).
+ *   - Every call on one GPU uses the same array, which keeps the last call's
+ *     contents (the quantize pass rewrites every byte the GEMM reads, so no
+ *     call depends on what an earlier one left). Calls that overlap on one
+ *     GPU, on streams not ordered against each other, race on it and give
+ *     undefined Y.
+ *   - The first call on a device looks up the array's device address there
+ *     (with that device current); a failure returns RFQ_ERR_HIP.
+ */
+rfq_status_t rfq_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                void* y, int y_dtype, int64_t ldy, rfq_stream_t stream);
+
+/* Bytes of the array rfq_linear_noalloc stages in (the largest
+ * rfq_linear_workspace_size it accepts). Host only. */
+size_t rfq_linear_noalloc_max_workspace(void);
 
 /* Static English text for a status code. Host only. */
 const char* rfq_status_string(rfq_status_t status);

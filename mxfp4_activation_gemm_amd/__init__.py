@@ -33,6 +33,8 @@ __all__ = [
     "backward_dx",
     "backward_dw",
     "linear",
+    "linear_noalloc",
+    "linear_noalloc_max_workspace",
     "linear_workspace_size",
     "library",
 ]
@@ -334,3 +336,21 @@ def linear(x, wq, sw, out_dtype=torch.bfloat16, out=None, workspace=None):
     check(load().rfq_linear(_ptr(x), _x_code(x), M, K, x.stride(0), _ptr(wq), _ptr(sw), N, _ptr(y), _y_code(y),
                             y.stride(0), _ptr(workspace), workspace.numel(), _stream()))
     return y
+
+
+def linear_noalloc_max_workspace():
+    return int(load().rfq_linear_noalloc_max_workspace())
+
+
+def linear_noalloc(x, wq, sw, out):
+    """The layer through rfq_linear_noalloc, for callers that cannot allocate:
+    `out` [M, N] (fp32 or bf16) is required, and Q(X), Q(R) are staged in the
+    library's own device array (at most linear_noalloc_max_workspace() bytes)."""
+    M, N, K = linear_shapes(x, wq, sw)
+    if out is None:
+        raise ValueError("out is required: this call allocates nothing")
+    check_out(out, M, N)
+    check_device(x.device, wq=wq, sw=sw, out=out)
+    check(load().rfq_linear_noalloc(_ptr(x), _x_code(x), M, K, x.stride(0), _ptr(wq), _ptr(sw), N, _ptr(out),
+                                    _y_code(out), out.stride(0), _stream()))
+    return out

@@ -267,6 +267,23 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                        static_cast<uint8_t*>(workspace), stream);
 }
 
+size_t rfq_linear_noalloc_max_workspace(void) { return rfq::kNoallocScratchBytes; }
+
+rfq_status_t rfq_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                void* y, int y_dtype, int64_t ldy, rfq_stream_t stream) {
+  RFQ_TRY(check_linear(x, x_dtype, M, K, ldx, w_codes, w_scales, N, y, y_dtype, ldy));
+  if (M == 0 || N == 0) return ok();
+  const size_t need = rfq_linear_workspace_size(M, K);
+  if (need > rfq::kNoallocScratchBytes)
+    return fail(RFQ_ERR_WORKSPACE_TOO_SMALL,
+                "M = %lld, K = %lld need %zu bytes of staging, beyond the %zu bytes of the allocation-free scratch",
+                (long long)M, (long long)K, need, rfq::kNoallocScratchBytes);
+  uint8_t* scratch = nullptr;
+  if (hipError_t e = rfq::noalloc_scratch(&scratch); e != hipSuccess) return launched(e);
+  return linear_launch(x, x_dtype, M, K, ldx, w_codes, w_scales, N, y, y_dtype, ldy, scratch, stream);
+}
+
 size_t rfq_backward_dx_workspace_size(int64_t N, int64_t K) {
   if (N <= 0 || N % 8 != 0 || N > kMaxK || K <= 0 || K % 32 != 0 || K > kMaxK) return 0;
   return round256((size_t)K * (size_t)N * 2);

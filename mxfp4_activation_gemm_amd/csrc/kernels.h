@@ -37,4 +37,10 @@ hipError_t launch_decode_transpose(const uint8_t* codes, const uint8_t* scales, 
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld_in, uint16_t* out,
                                  int64_t ld_out, hipStream_t stream);
 
+// Staging memory of the allocation-free linear entry point (noalloc.hip):
+// the device address, on the current device, of a library-owned array of
+// kNoallocScratchBytes (looked up once per device and kept).
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(uint8_t** ptr);
+
 }  // namespace rfq

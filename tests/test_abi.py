@@ -36,11 +36,11 @@ def declared_functions():
 
 def test_header_declarations_are_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
-    assert lib.rfq_abi_version() == 5
+    assert lib.rfq_abi_version() == 6
 
 
 def status_name(st):
@@ -197,3 +197,24 @@ def test_backward_validation(lib):
     assert bw(od=3) == "RFQ_ERR_UNSUPPORTED_DTYPE"
     assert bw(N=0, dy=None, qx=None, qr=None, out=None, ws=None) == "RFQ_OK"
 
+
+def test_linear_noalloc_validation(lib):
+    f = lib.rfq_linear_noalloc
+    cap = lib.rfq_linear_noalloc_max_workspace()
+    assert cap == 64 << 20
+
+    def na(x=FAKE, dt=0, M=8, K=64, ldx=64, w=FAKE, sw=FAKE, N=8, y=FAKE, yd=1, ldy=8):
+        return status_name(f(x, dt, M, K, ldx, w, sw, N, y, yd, ldy, None))
+    assert na(x=None) == "RFQ_ERR_NULL_POINTER"
+    assert na(w=None) == "RFQ_ERR_NULL_POINTER"
+    assert na(K=48, ldx=48) == "RFQ_ERR_INVALID_SHAPE"
+    assert na(ldx=60) == "RFQ_ERR_INVALID_STRIDE"
+    assert na(ldy=4) == "RFQ_ERR_INVALID_STRIDE"
+    assert na(yd=7) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert na(x=FAKE + 8) == "RFQ_ERR_MISALIGNED"
+    # a shape whose staging exceeds the library's array is refused on the host
+    # (12400 x 5120 needs 67.5 MB > 64 MiB) before the device is touched
+    assert lib.rfq_linear_workspace_size(12400, 5120) > cap
+    assert na(M=12400, K=5120, ldx=5120) == "RFQ_ERR_WORKSPACE_TOO_SMALL"
+    assert "allocation-free" in lib.rfq_last_error_detail().decode()
+    assert na(M=0, x=None, w=None, sw=None, y=None) == "RFQ_OK"

@@ -97,6 +97,7 @@ def test_linear_rejects(case, match):
     elif case == "x_3d":
         x = torch.zeros((1, M, K), dtype=torch.bfloat16)
     raises(lambda: rfq.linear(x, wq, sw, out=out, workspace=ws), match)
+    raises(lambda: rfq.linear_noalloc(x, wq, sw, out), match)
 
 
 @pytest.mark.parametrize("case,match", [
