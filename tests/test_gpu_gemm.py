@@ -270,42 +270,59 @@ def test_streamed_tiles_every_output(M, N, K, out_dtype):
 
 
 @pytest.mark.parametrize("name", ["qwen3vl_attn_proj", "qwen3vl_ffn_up", "wan22_ffn", "dit_ffn_down"])
-def test_full_size_config_sampled(name):
-    """The configuration as the benchmark runs it (full X, full W, bf16 Y, one
-    rfq_linear call); the oracle checks a sample of rows of Q(X), Q(R) and of
-    the weight codes bit for bit, and the outputs at sampled rows x sampled
-    columns."""
+def test_full_size_config(name):
+    """The configuration as the benchmark runs it (full X, full W, one
+    rfq_linear call, on the streamed-tile path wherever the benchmark takes
+    it):
+      * Q(X), Q(R) and their scales, as left in the workspace, byte-equal to
+        the oracle over the WHOLE tensor (the oracle runs in row chunks on a
+        CPU process pool while the GPU works);
+      * the weight's codes and scales at sampled rows;
+      * Y at 128 sampled rows x 256 sampled columns, both as bf16 Y (the
+        benchmark's output) and as fp32 Y from a second call, the latter at
+        the plain 1e-5 S + 2^-126 gate (with K/128 fp32 accumulations per
+        product: 80 at K = 5120, 216 at K = 13824)."""
+    import oracle_pool
     cfg = workloads.CONFIGS[name]
-    log(f"[gemm] full size {name} M={cfg.M} N={cfg.N} K={cfg.K}: generating")
-    xb = workloads.x_bf16(cfg)
-    wb = workloads.w_bf16(cfg)
-    x, w = dev_bf16(xb), dev_bf16(wb)
-    log("   running on the GPU")
-    wq, sw = rfq.quantize_mxfp4(w)
-    ws = torch.empty(rfq.linear_workspace_size(cfg.M, cfg.K), dtype=torch.uint8, device="cuda")
-    y = rfq.linear(x, wq, sw, out_dtype=torch.bfloat16, workspace=ws)
-    torch.cuda.synchronize()
-    rows = workloads.sample_rows(cfg, n_random=126)
-    cols = np.unique(np.concatenate([[0, cfg.N - 1],
-                                     np.random.default_rng(cfg.seed).choice(cfg.N, 254, replace=False)]))
-    M, K = cfg.M, cfg.K
-    r256 = lambda b: (b + 255) // 256 * 256
-    c, s = r256(M * K // 2), r256(M * K // 32)
-    wsh = host(ws)
-    gqx = wsh[:M * K // 2].reshape(M, K // 2)[rows]
-    gsx = wsh[c:c + M * K // 32].reshape(M, K // 32)[rows]
-    gqr = wsh[c + s:c + s + M * K // 2].reshape(M, K // 2)[rows]
-    gsr = wsh[2 * c + s:2 * c + s + M * K // 32].reshape(M, K // 32)[rows]
-    log(f"   oracle on {len(rows)} rows x {len(cols)} columns")
-    oqx, osx, oqr, osr = oracle_rfq(xb[rows])
-    assert_bytes_equal(gqx, oqx, "Q(X) sampled rows")
-    assert_bytes_equal(gsx, osx, "SX sampled rows")
-    assert_bytes_equal(gqr, oqr, "Q(R) sampled rows")
-    assert_bytes_equal(gsr, osr, "SR sampled rows")
-    owq, osw = oracle_mx(wb[cols])
-    assert_bytes_equal(host(wq)[cols], owq, "W codes sampled rows")
-    assert_bytes_equal(host(sw)[cols], osw, "W scales sampled rows")
-    y_ref, s_ref = oracle_y(xb[rows], wb[cols])
-    yh = host_bf16_as_f64(y)[np.ix_(rows, cols)]
-    worst = check_y(yh, y_ref, s_ref, torch.bfloat16, name)
-    log(f"   ok, max |dY|/S = {worst:.2e}")
+    log(f"[gemm] full size {name} M={cfg.M} N={cfg.N} K={cfg.K}: oracle codes on {oracle_pool.workers()} "
+        f"processes; generating inputs")
+    codes_job = oracle_pool.RfqCodesFull(cfg)
+    try:
+        xb = workloads.x_bf16(cfg)
+        wb = workloads.w_bf16(cfg)
+        x, w = dev_bf16(xb), dev_bf16(wb)
+        log("   running on the GPU")
+        wq, sw = rfq.quantize_mxfp4(w)
+        del w
+        ws = torch.empty(rfq.linear_workspace_size(cfg.M, cfg.K), dtype=torch.uint8, device="cuda")
+        y = rfq.linear(x, wq, sw, out_dtype=torch.bfloat16, workspace=ws)
+        y32 = rfq.linear(x, wq, sw, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        rows = workloads.sample_rows(cfg, n_random=126)
+        cols = np.unique(np.concatenate([[0, cfg.N - 1],
+                                         np.random.default_rng(cfg.seed).choice(cfg.N, 254, replace=False)]))
+        M, K = cfg.M, cfg.K
+        r256 = lambda b: (b + 255) // 256 * 256
+        c, s = r256(M * K // 2), r256(M * K // 32)
+        wsh = host(ws)
+        yh = host_bf16_as_f64(y)[np.ix_(rows, cols)]
+        y32h = host(y32)[np.ix_(rows, cols)].astype(np.float64)
+        del ws, y, y32, x
+        log(f"   oracle Y on {len(rows)} rows x {len(cols)} columns")
+        owq, osw = oracle_mx(wb[cols])
+        assert_bytes_equal(host(wq)[cols], owq, "W codes sampled rows")
+        assert_bytes_equal(host(sw)[cols], osw, "W scales sampled rows")
+        y_ref, s_ref = oracle_y(xb[rows], wb[cols])
+        worst = check_y(yh, y_ref, s_ref, torch.bfloat16, f"{name} bf16 Y")
+        worst32 = check_y(y32h, y_ref, s_ref, torch.float32, f"{name} fp32 Y")
+        log(f"   Y ok: max |dY|/S = {worst:.2e} (bf16 Y), {worst32:.2e} (fp32 Y)")
+        del xb, wb
+        log("   waiting for the oracle's codes of all rows")
+        oqx, osx, oqr, osr = codes_job.result(timeout=600)
+    finally:
+        codes_job.close()
+    assert_bytes_equal(wsh[:M * K // 2].reshape(M, K // 2), oqx, "Q(X) codes, all rows")
+    assert_bytes_equal(wsh[c:c + M * K // 32].reshape(M, K // 32), osx, "Q(X) scales, all rows")
+    assert_bytes_equal(wsh[c + s:c + s + M * K // 2].reshape(M, K // 2), oqr, "Q(R) codes, all rows")
+    assert_bytes_equal(wsh[2 * c + s:2 * c + s + M * K // 32].reshape(M, K // 32), osr, "Q(R) scales, all rows")
+    log(f"   Q(X), Q(R) and scales byte-equal on all {M} rows")
