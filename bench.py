@@ -250,7 +250,12 @@ def layer_timings(rfq, torch, cfg, x, wq, sw, batch_ms, reps):
     def step():
         quantize()
         gemm()
+
+    def fused():
+        rfq._lib.check(lib.rfq_linear_fused(x.data_ptr(), 0, M, K, x.stride(0), wq.data_ptr(), sw.data_ptr(), N,
+                                            y.data_ptr(), yd, N, sp))
     q_ms, g_ms, s_ms = batch_ms(quantize, reps), batch_ms(gemm, reps), batch_ms(step, reps)
+    f_ms = batch_ms(fused, reps) if K % 512 == 0 else None
     flops = 4.0 * M * N * K
     return {
         "M": M, "K": K, "N": N, "y_dtype": cfg.y_dtype,
@@ -261,6 +266,8 @@ def layer_timings(rfq, torch, cfg, x, wq, sw, batch_ms, reps):
         "gemm_pct_fp4_peak": round(100 * flops / (g_ms * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 2),
         "quantize_us": round(q_ms * 1e3, 2),
         "quantize_GB_per_s": round(QUANT_BYTES_PER_ELEM * M * K / (q_ms * 1e-3) / 1e9, 1),
+        "fused_step_us": round(f_ms * 1e3, 2) if f_ms else None,
+        "fused_over_two_kernel_step": round(f_ms / s_ms, 3) if f_ms else None,
         "reps": reps,
     }
 
@@ -382,6 +389,14 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     quant_gbs = QUANT_BYTES_PER_ELEM * M * K / (quant_ms * 1e-3) / 1e9
+
+    # the layer with the quantization inside the GEMM (rfq_linear_fused: one
+    # launch, Q(X) and Q(R) never leave the GEMM) beside the two-kernel step
+    def fused_step():
+        rfq._lib.check(lib.rfq_linear_fused(x.data_ptr(), 0, M, K, x.stride(0), wq.data_ptr(), sw.data_ptr(), N,
+                                            y.data_ptr(), rfq._lib.DTYPE_BF16, N, sp))
+    fused_ms = batch_ms(fused_step, 50, warm=10) if K % 512 == 0 else None
+    two_kernel_ms = batch_ms(step, 50, warm=10)
 
     # plain W4A4 GEMM (no residual operand) on the same operands, for the
     # overhead of the residual path
@@ -543,6 +558,14 @@ def main():
                 "pct_bf16_peak": round(100 * 4.0 * M * N * K / (bdw_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
                 "what": "dW = dY^T (deq Q(X) + deq Q(R)) (rfq_backward_dw: transposes of dY, Q(X), Q(R), then the "
                         "K-doubled bf16 GEMM with transposed store), bf16 dW",
+            },
+            "rfq_linear_fused": {
+                "avg_call_us": round(fused_ms * 1e3, 2) if fused_ms else None,
+                "TFLOP_per_s": round(flops / (fused_ms * 1e-3) / 1e12, 1) if fused_ms else None,
+                "two_kernel_step_us": round(two_kernel_ms * 1e3, 2),
+                "fused_over_two_kernel": round(fused_ms / two_kernel_ms, 3) if fused_ms else None,
+                "what": "the layer with Q(X), Q(R) formed inside the GEMM from bf16 X tiles (one launch, 128 x 256 "
+                        "tiles), against the quantize pass + GEMM step, same launches back to back",
             },
             "gemm_plain_w4a4": {
                 "avg_launch_us": round(w4a4_ms * 1e3, 2),

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RFQ_ABI_VERSION 6
+#define RFQ_ABI_VERSION 7
 
 typedef enum rfq_status {
   RFQ_OK = 0,
@@ -267,6 +267,27 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                         const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                         void* y, int y_dtype, int64_t ldy,
                         void* workspace, size_t workspace_bytes, rfq_stream_t stream);
+
+/*
+ * rfq_linear_fused - the whole layer with the quantization inside the GEMM
+ * ("Activation Outliers Matter", §1 contributions: the residual is
+ * re-quantized during the GEMM and its contribution accumulated). The GEMM
+ * reads bf16 X tiles and, for each K stage of each output tile, forms Q(X),
+ * R = X - deq(Q(X)) and Q(R) itself (the same encoding as
+ * rfq_residual_quantize) in registers and LDS; Q(X) and Q(R) are never
+ * written to memory and no workspace is needed. Y is the same as
+ * rfq_linear's, bit for bit: same codes, same accumulation order.
+ *   x [M, K] bf16 only (x_dtype RFQ_DTYPE_BF16), row stride ldx elements,
+ *     ldx < 2^24;
+ *   K a multiple of 512 (whole scale groups of the weight);
+ *   other arguments as rfq_linear.
+ * Errors as rfq_linear, plus RFQ_ERR_UNSUPPORTED_DTYPE for fp32 X and
+ * RFQ_ERR_INVALID_SHAPE for K % 512 != 0, RFQ_ERR_INVALID_STRIDE for
+ * ldx >= 2^24.
+ */
+rfq_status_t rfq_linear_fused(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                              const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                              void* y, int y_dtype, int64_t ldy, rfq_stream_t stream);
 
 /*
  * rfq_linear_noalloc - rfq_linear for callers that cannot allocate memory:

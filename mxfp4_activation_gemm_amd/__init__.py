@@ -33,6 +33,7 @@ __all__ = [
     "backward_dx",
     "backward_dw",
     "linear",
+    "linear_fused",
     "linear_noalloc",
     "linear_noalloc_max_workspace",
     "linear_workspace_size",
@@ -335,6 +336,22 @@ def linear(x, wq, sw, out_dtype=torch.bfloat16, out=None, workspace=None):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     check(load().rfq_linear(_ptr(x), _x_code(x), M, K, x.stride(0), _ptr(wq), _ptr(sw), N, _ptr(y), _y_code(y),
                             y.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def linear_fused(x, wq, sw, out_dtype=torch.bfloat16, out=None):
+    """The layer with Q(X) and Q(R) formed inside the GEMM (rfq_linear_fused):
+    bf16 X [M, K] with K a multiple of 512; no workspace; Y bit-equal to linear()."""
+    M, N, K = linear_shapes(x, wq, sw)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x: the in-GEMM quantization takes bf16 X only")
+    if K % 512:
+        raise ValueError(f"K = {K}: the in-GEMM quantization needs K a multiple of 512")
+    _given_out(out, M, N)
+    check_device(x.device, wq=wq, sw=sw, out=out)
+    y = _new_out(out, M, N, out_dtype, x.device)
+    check(load().rfq_linear_fused(_ptr(x), DTYPE_BF16, M, K, x.stride(0), _ptr(wq), _ptr(sw), N, _ptr(y),
+                                  _y_code(y), y.stride(0), _stream()))
     return y
 
 

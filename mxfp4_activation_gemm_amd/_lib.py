@@ -31,6 +31,7 @@ SIGNATURES = {
     "rfq_gemm_w4a4": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _i64, _p]),
     "rfq_linear_workspace_size": (_sz, [_i64, _i64]),
     "rfq_linear": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _i64, _p, _i, _i64, _p, _sz, _p]),
+    "rfq_linear_fused": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _i64, _p, _i, _i64, _p]),
     "rfq_linear_noalloc": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _i64, _p, _i, _i64, _p]),
     "rfq_linear_noalloc_max_workspace": (_sz, []),
     "rfq_status_string": (ctypes.c_char_p, [_i]),

@@ -267,6 +267,21 @@ rfq_status_t rfq_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                        static_cast<uint8_t*>(workspace), stream);
 }
 
+rfq_status_t rfq_linear_fused(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                              const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                              void* y, int y_dtype, int64_t ldy, rfq_stream_t stream) {
+  RFQ_TRY(check_linear(x, x_dtype, M, K, ldx, w_codes, w_scales, N, y, y_dtype, ldy));
+  if (x_dtype != RFQ_DTYPE_BF16)
+    return fail(RFQ_ERR_UNSUPPORTED_DTYPE, "x_dtype %d: the in-GEMM quantization takes bf16 X only", x_dtype);
+  if (K % 512 != 0)
+    return fail(RFQ_ERR_INVALID_SHAPE, "K = %lld: the in-GEMM quantization needs K a multiple of 512", (long long)K);
+  if (ldx >= (int64_t(1) << 24))
+    return fail(RFQ_ERR_INVALID_STRIDE, "ldx = %lld: the in-GEMM quantization needs ldx < 2^24", (long long)ldx);
+  if (M == 0 || N == 0) return ok();
+  return launched(rfq::launch_gemm_fused(static_cast<const uint16_t*>(x), ldx, w_codes, w_scales, M, N, K, y,
+                                         y_dtype == RFQ_DTYPE_BF16, ldy, static_cast<hipStream_t>(stream)));
+}
+
 size_t rfq_linear_noalloc_max_workspace(void) { return rfq::kNoallocScratchBytes; }
 
 rfq_status_t rfq_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,

@@ -60,6 +60,7 @@
 //    and N tiles; partial K is masked per 16-byte chunk.
 
 #include "kernels.h"
+#include "mx_encode.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -105,16 +106,22 @@ constexpr int kGroupM = 4;                          // tile rows swept together 
 // 32x32x16 MFMA, whose 16-byte fragments are read exactly like the E2M1
 // ones. kT: the result is stored transposed (element (r, c) of the tile to
 // y[c * ldy + r]).
-template <int kX, int kR, bool kT = false>
+//
+// kQ: the activation arrives as bf16 X and the GEMM quantizes it itself (X
+// and its residual R to MXFP4, the RFQ encoding), stage by stage, into the
+// LDS ring; the weight side is unchanged. Each stage slot then also holds
+// the activation's scale bytes of that stage ([rows, 4] per term).
+template <int kX, int kR, bool kT = false, bool kQ = false>
 struct Fmts {
   static constexpr int kXFmt = kX, kRFmt = kR;
   static constexpr bool kResid = kR != 0;
   static constexpr bool kBf16 = kX == 16;
   static constexpr bool kOutT = kT;
+  static constexpr bool kFusedQ = kQ;
   static constexpr int kXSub = kX == 8 ? 2 : 1;
   static constexpr int kRSub = kR == 8 ? 2 : (kR != 0 ? 1 : 0);
   static constexpr int kSubA = kXSub + kRSub;          // activation sub-tiles per stage
-  static constexpr int kScalesA = kBf16 ? 0 : (kResid ? 2 : 1);   // activation scale streams
+  static constexpr int kScalesA = (kBf16 || kQ) ? 0 : (kResid ? 2 : 1);   // activation scale streams (group-wise)
   static constexpr int kScalesB = kBf16 ? 0 : 1;       // weight scale stream
   static constexpr int kTerms = kResid ? 2 : 1;        // MFMAs per output tile per step
   // E2M1 x E2M1 products run on the 16 x 16 x 128 form of the scaled MFMA
@@ -124,6 +131,7 @@ struct Fmts {
                     (kX == 16 && (kR == 0 || kR == 16)),
                 "formats");
   static_assert(!kT || kBf16, "transposed stores are for the bf16 products");
+  static_assert(!kQ || (kX == 4 && kR == 4 && !kT), "in-GEMM quantization is of the RFQ operands");
 };
 using FmtW4A4 = Fmts<4, 0>;
 using FmtRfq = Fmts<4, 4>;
@@ -131,6 +139,7 @@ using FmtW4A8 = Fmts<8, 0>;
 using FmtRfq8 = Fmts<4, 8>;
 using FmtBf16 = Fmts<16, 0>;                // dX = dY Wd: bf16 x bf16
 using FmtBf16PairT = Fmts<16, 16, true>;    // dW^T = Xq dY^T + Xr dY^T, stored as dW
+using FmtRfqFused = Fmts<4, 4, false, true>;  // RFQ from bf16 X, quantized inside the GEMM
 
 // MFMA format code of an element format: E4M3 is 0, E2M1 is 4.
 template <int kFmt>
@@ -147,7 +156,14 @@ struct TileCfg {
   static constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;           // MFMA tiles per wave
   static constexpr int kT16M = kWaveM / 16, kT16N = kWaveN / 16;       // the same in 16 x 16 tiles
   static constexpr int kTileBytesA = kBM * kRowBytes, kTileBytesB = kBN * kRowBytes;   // one sub-tile
-  static constexpr int kStageBytes = F::kSubA * kTileBytesA + kTileBytesB;
+  // in-GEMM quantization: the stage's activation scale bytes, [kBM, 4] for
+  // X then for R, after the code sub-tiles
+  static constexpr int kStageScaleOff = F::kSubA * kTileBytesA + kTileBytesB;
+  static constexpr int kStageScaleBytes = F::kFusedQ ? 2 * kBM * 4 : 0;
+  static constexpr int kStageBytes = kStageScaleOff + kStageScaleBytes;
+  // in-GEMM quantization: 16-byte loads of bf16 X per lane per stage (4
+  // lanes per 32-block, 4 blocks per stage row), 4 rows per wave per load
+  static constexpr int kLoadsX = F::kFusedQ ? kBM * 16 / (64 * kWaves) : 0;
   static constexpr int kScaleBytesA = kBM * kScaleRowBytes;
   static constexpr int kScaleBytes = F::kScalesA * kScaleBytesA + F::kScalesB * kBN * kScaleRowBytes;
   static constexpr int kLdsBytes = kRing * kStageBytes + kScaleBytes;
@@ -161,6 +177,8 @@ struct TileCfg {
   static_assert(kTM >= 1 && kTN >= 1 && kLoadsA >= 1 && kLoadsB >= 1, "tile shape");
   static_assert(!F::kM16 || (kT16M % 2 == 0 && kT16N % 2 == 0), "16 x 16 tiles come in halves");
   static_assert(kLdsBytes * kOcc <= 160 * 1024, "LDS budget per CU");
+  static_assert(kStageBytes % 16 == 0, "stage slots 16-byte aligned");
+  static_assert(!F::kFusedQ || (kLoadsX * 4 * kWaves == kBM && kBM % (4 * kWaves) == 0), "X load mapping");
 };
 // Main tiles: 256 x 256 outputs, 8 waves of 64 x 128 (128 accumulators
 // each), one workgroup per CU (up to 156 KB of LDS); for the last partial
@@ -169,7 +187,7 @@ struct TileCfg {
 // residual (three activation sub-tiles) the stage would not fit three deep,
 // so that variant uses 128 x 256 tiles (8 waves of 32 x 128) and 64 x 128
 // quadrants.
-template <class F, bool kNarrow = (F::kSubA > 2)>
+template <class F, bool kNarrow = (F::kSubA > 2 || F::kFusedQ)>
 struct Tiles {
   using Big = TileCfg<256, 256, 8, 1, F>;
   using Quad = TileCfg<128, 128, 4, 2, F>;
@@ -178,6 +196,8 @@ struct Tiles {
 };
 template <class F>
 struct Tiles<F, true> {
+  // (in-GEMM quantization needs registers for the bf16 X tiles in flight, so
+  // it also runs 128-row tiles)
   using Big = TileCfg<128, 256, 8, 1, F>;
   using Quad = TileCfg<64, 128, 4, 2, F>;
   using Half = Big;                          // (not used)
@@ -193,6 +213,7 @@ struct GemmParams {
   const uint8_t* sw;
   void* y;
   int64_t ldy;
+  int64_t ldx;            // in-GEMM quantization: row stride of bf16 X (at qx), elements
   int32_t M, N, K;
   // Tile map: `grid` work items; tiles of gm x gn form a tiles_m x tiles_n
   // grid walked in a fixed logical order; item ids map to logical tile
@@ -376,9 +397,11 @@ __device__ __forceinline__ uint32_t gather_stage_bytes(i32x4_t w, uint32_t sel01
 
 // One group of 16 x 16 x 128 MFMAs: weight half HW (kHN fragments of 16
 // rows) against activation half HX (kHM row tiles, kTerms terms each), at
-// stage P of the scale group (the scale byte op_sel picks). Terms outermost,
-// so MFMAs into one accumulator are kHM x kHN instructions apart.
-template <int P, int HW, int HX, int kTerms, int kHM, int kHN, int kT16M, int kT16N>
+// stage P of the scale group (the weight scale byte op_sel picks; PX for the
+// activation's, which is byte 0 when the GEMM quantizes the activation
+// itself and holds per-stage scale bytes). Terms outermost, so MFMAs into
+// one accumulator are kHM x kHN instructions apart.
+template <int P, int PX, int HW, int HX, int kTerms, int kHM, int kHN, int kT16M, int kT16N>
 __device__ __forceinline__ void mfma16_group(f32x4_t (&acc)[kT16M][kT16N], const i32x4_t (&wf)[2][kHN],
                                              const i32x4_t (&xf)[2][kHM * kTerms], const uint32_t (&ws)[2][kHN],
                                              const uint32_t (&xs)[2][kHM * kTerms]) {
@@ -390,7 +413,7 @@ __device__ __forceinline__ void mfma16_group(f32x4_t (&acc)[kT16M][kT16N], const
       for (int n = 0; n < kHN; ++n)
         acc[HX * kHM + m][HW * kHN + n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             widen(wf[HW][n]), widen(xf[HX][m * kTerms + t]), acc[HX * kHM + m][HW * kHN + n], 4, 4, P,
-            (int)ws[HW][n], P, (int)xs[HX][m * kTerms + t]);
+            (int)ws[HW][n], PX, (int)xs[HX][m * kTerms + t]);
 }
 
 // kFast: K % 512 == 0 (whole stages and whole 16-block scale groups); the
@@ -435,20 +458,29 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // as zero), one per activation sub-tile: an E4M3 term's second sub-tile
   // starts 32 bytes (two chunks) into the row, so the same offsets fetch it.
   const uint32_t kbytes = (uint32_t)p.K / 2, kblocks = (uint32_t)p.K / 32;
-  __amdgpu_buffer_rsrc_t ra[kSubA], rw, rsx, rsr, rsw;
+  __amdgpu_buffer_rsrc_t ra[kSubA], rw, rsx, rsr, rsw, rx;
   auto set_load_tile = [&](const GemmParams& q, int m0, int n0) __attribute__((always_inline)) {
     const uint32_t rows_a = (uint32_t)min(kBM, q.M - m0), rows_b = (uint32_t)min(kBN, q.N - n0);
-    const uint32_t xrow = F::kXFmt == 8 ? 2 * kbytes : kbytes, rrow = F::kRFmt == 8 ? 2 * kbytes : kbytes;
-    ra[0] = make_rsrc(q.qx + (int64_t)m0 * xrow, rows_a * xrow);
-    if constexpr (F::kXFmt == 8) ra[1] = make_rsrc(q.qx + (int64_t)m0 * xrow + 32, rows_a * xrow - 32);
-    if constexpr (F::kResid) {
-      ra[F::kXSub] = make_rsrc(q.qr + (int64_t)m0 * rrow, rows_a * rrow);
-      if constexpr (F::kRFmt == 8) ra[F::kXSub + 1] = make_rsrc(q.qr + (int64_t)m0 * rrow + 32, rows_a * rrow - 32);
+    if constexpr (F::kFusedQ) {
+      // bf16 X rows [m0, m0 + rows_a): the extent ends at the last row's K-th
+      // element, so a lane offset that carries a row past the tile's last
+      // reads zeros
+      rx = make_rsrc(q.qx + (int64_t)m0 * q.ldx * 2, (uint32_t)(((int64_t)(rows_a - 1) * q.ldx + q.K) * 2));
+    } else {
+      const uint32_t xrow = F::kXFmt == 8 ? 2 * kbytes : kbytes, rrow = F::kRFmt == 8 ? 2 * kbytes : kbytes;
+      ra[0] = make_rsrc(q.qx + (int64_t)m0 * xrow, rows_a * xrow);
+      if constexpr (F::kXFmt == 8) ra[1] = make_rsrc(q.qx + (int64_t)m0 * xrow + 32, rows_a * xrow - 32);
+      if constexpr (F::kResid) {
+        ra[F::kXSub] = make_rsrc(q.qr + (int64_t)m0 * rrow, rows_a * rrow);
+        if constexpr (F::kRFmt == 8) ra[F::kXSub + 1] = make_rsrc(q.qr + (int64_t)m0 * rrow + 32, rows_a * rrow - 32);
+      }
     }
     rw = make_rsrc(q.w + (int64_t)n0 * kbytes, rows_b * kbytes);
     if constexpr (!F::kBf16) {
-      rsx = make_rsrc(q.sx + (int64_t)m0 * kblocks, rows_a * kblocks);
-      rsr = make_rsrc(kResid ? q.sr + (int64_t)m0 * kblocks : q.sx, rows_a * kblocks);
+      if constexpr (!F::kFusedQ) {
+        rsx = make_rsrc(q.sx + (int64_t)m0 * kblocks, rows_a * kblocks);
+        rsr = make_rsrc(kResid ? q.sr + (int64_t)m0 * kblocks : q.sx, rows_a * kblocks);
+      }
       rsw = make_rsrc(q.sw + (int64_t)n0 * kblocks, rows_b * kblocks);
     }
   };
@@ -482,7 +514,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     return fmt == 8 ? lda_row[n] * (2 * kbytes) + 64 * (lda_chunk[n] >> 1) + 16 * (lda_chunk[n] & 1)
                     : lda_row[n] * kbytes + 16 * lda_chunk[n];
   };
-  constexpr int kDmaPerStage = kSubA * C::kLoadsA + C::kLoadsB;
+  constexpr int kDmaPerStage = (F::kFusedQ ? 0 : kSubA * C::kLoadsA) + C::kLoadsB;
+  constexpr int kLoadsX = C::kLoadsX;
   constexpr int kMfmaPerStep = kTM * kTN * F::kTerms;
   constexpr int kReadsPerStep = kTM * kSubA + kTN;
   constexpr int kScaleRowReads = kTM * F::kScalesA + kTN;
@@ -510,7 +543,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     const bool past_end = st >= total_stages;
     const uint32_t kst_s = past_end ? 0u : (uint32_t)kst;   // kFast: stage in the scalar offset
 #pragma unroll
-    for (int n = 0; n < C::kLoadsA; ++n) {
+    for (int n = 0; n < (F::kFusedQ ? 0 : C::kLoadsA); ++n) {
       uint8_t* dst = buf + (kBM / kWaves * wave + 16 * n) * kRowBytes;
 #pragma unroll
       for (int t = 0; t < kSubA; ++t) {
@@ -540,7 +573,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
         so = 0;
         if ((uint32_t)kst * (kBK / 32) + ldb_chunk[n] >= kblocks || past_end) vo = kOOB;
       }
-      const int ix = kSubA * C::kLoadsA + n;
+      const int ix = (F::kFusedQ ? 0 : kSubA * C::kLoadsA) + n;
       if (part == 2 || (ix < kPart0) == (part == 0))
         load16_to_lds(rw, buf + kSubA * kTileBytesA + ldb_group_row(n) * kRowBytes, vo, so);
     }
@@ -581,13 +614,77 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
 #pragma unroll
     for (int t = 0; t < kScaleLoadsPerWave; ++t) {
       const int j = (kScaleLoadsPerWave * (int)wave + t) % (kPieces > 0 ? kPieces : 1);   // wave-uniform
-      if (j < kPiecesA)
+      // pieces 0 .. kScalesA kPiecesA - 1 are the activation's (none when the
+      // GEMM quantizes the activation itself), the rest the weight's
+      if (F::kScalesA >= 1 && j < kPiecesA)
         issue_scale_piece(rsx, g, 0, j);
-      else if (kResid && j < 2 * kPiecesA)
+      else if (F::kScalesA >= 2 && j < 2 * kPiecesA)
         issue_scale_piece(rsr, g, 1, j - kPiecesA);
       else
         issue_scale_piece(rsw, g, F::kScalesA, j - F::kScalesA * kPiecesA);
     }
+  };
+
+  // In-GEMM quantization of the activation (F::kFusedQ). Stage st + 2's
+  // bf16 X tile (kBM rows x 128 elements) is loaded into registers at the
+  // start of stage st, beside that stage's second weight part, and quantized
+  // after stage st's barrier (spread over its last two MFMA groups) into its
+  // ring slot, which is free since the barrier of stage st - 1: RFQ codes of
+  // X and of R = X - deq(Q(X)) in the layout the DMA would have written
+  // (chunk c of row r at c ^ f(r)), and the stage's scale bytes; the barrier
+  // of stage st + 1 makes them visible before stage st + 2's first reads.
+  // Lane (quad q = lane / 4, part p = lane % 4) of wave w takes, in load u,
+  // row (kBM / kWaves) w + 4 u + q / 4 of the tile, block q % 4 of the stage
+  // and its elements 8 p .. 8 p + 7, so each quad holds one 32-block (the
+  // DPP block maxima need that).
+  mx::u32x4_t xin[kLoadsX > 0 ? kLoadsX : 1];      // bf16 X of the stage being quantized
+  uint32_t xld_off[kLoadsX > 0 ? kLoadsX : 1];
+  if constexpr (F::kFusedQ) {
+#pragma unroll
+    for (int u = 0; u < kLoadsX; ++u) {
+      const uint32_t row = kBM / kWaves * wave + 4 * u + (lane >> 4);
+      xld_off[u] = (uint32_t)(row * p.ldx * 2) + (32 * ((lane >> 2) & 3) + 8 * (lane & 3)) * 2;
+    }
+  }
+  auto issue_x = [&](int st) __attribute__((always_inline)) {
+    if constexpr (F::kFusedQ) {
+      // the stage's K offset in the scalar offset; past the end of the stream,
+      // the tile's stage 0 again (nothing reads what it becomes)
+      const uint32_t so = st >= total_stages ? 0u : (uint32_t)(st - load_base) * (kBK * 2);
+#pragma unroll
+      for (int u = 0; u < kLoadsX; ++u)
+        xin[u] = __builtin_bit_cast(mx::u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xld_off[u], so, 0));
+    }
+  };
+  // units [u0, u1) of stage st's X (register set `set`)
+  auto quantize_units = [&](int st, auto u0_c, auto u1_c) __attribute__((always_inline)) {
+    if constexpr (F::kFusedQ) {
+      constexpr int u0 = decltype(u0_c)::value, u1 = decltype(u1_c)::value;
+      uint8_t* slot = ring + (st % kRing) * kStageBytes;
+      const uint32_t blk = (lane >> 2) & 3, part = lane & 3;
+#pragma unroll
+      for (int u = u0; u < u1; ++u) {
+        const mx::RfqLane e = mx::rfq_encode_bf16x8(xin[u]);
+        const uint32_t row = kBM / kWaves * wave + 4 * u + (lane >> 4);
+        const uint32_t off = row * kRowBytes + 16 * (blk ^ swz(row)) + 4 * part;
+        *reinterpret_cast<uint32_t*>(slot + off) = e.cx;
+        *reinterpret_cast<uint32_t*>(slot + kTileBytesA + off) = e.cr;
+        if (part == 0) {
+          slot[C::kStageScaleOff + row * 4 + blk] = (uint8_t)e.sx;
+          slot[C::kStageScaleOff + kBM * 4 + row * 4 + blk] = (uint8_t)e.sr;
+        }
+      }
+    }
+  };
+  auto quantize_x = [&](int st) __attribute__((always_inline)) {
+    quantize_units(st, std::integral_constant<int, 0>{}, std::integral_constant<int, kLoadsX>{});
+  };
+  // half h of stage st's units (the loop spreads a stage's quantization over
+  // two MFMA groups)
+  auto quantize_half = [&](int st, auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    quantize_units(st, std::integral_constant<int, h * kLoadsX / 2>{},
+                   std::integral_constant<int, (h + 1) * kLoadsX / 2>{});
   };
 
   // Per-lane LDS read offsets: lane (lhalf, lrow) of a 32-row fragment reads
@@ -680,7 +777,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   };
   auto read_xs16 = [&](auto h_c) __attribute__((always_inline)) {
     constexpr int h = decltype(h_c)::value;
-    if constexpr (!F::kBf16) {
+    if constexpr (!F::kBf16 && !F::kFusedQ) {
 #pragma unroll
       for (int m = 0; m < kHM; ++m) {
         const uint32_t row = a_row0 + 16 * (h * kHM + m) + (lane & 15);
@@ -688,6 +785,21 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
         for (int t = 0; t < F::kTerms; ++t)
           xs[h][m * F::kTerms + t] = gather_stage_bytes(
               *reinterpret_cast<const i32x4_t*>(sbuf + t * kScaleBytesA + row * kScaleRowBytes), sel01);
+      }
+    }
+  };
+
+  // In-GEMM quantization: the activation scale bytes of stage st, one byte
+  // per fragment (row lane % 16, block lane / 16 of the stage), for op_sel 0.
+  auto read_xs16f = [&](int st, auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    if constexpr (F::kFusedQ) {
+      const uint8_t* sc = ring + (st % kRing) * kStageBytes + C::kStageScaleOff + (lane >> 4);
+#pragma unroll
+      for (int m = 0; m < kHM; ++m) {
+        const uint32_t row = a_row0 + 16 * (h * kHM + m) + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < F::kTerms; ++t) xs[h][m * F::kTerms + t] = sc[t * kBM * 4 + row * 4];
       }
     }
   };
@@ -714,12 +826,29 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   zero_acc();
 
   // Prologue: scales of group 0, then stages 0..2; wait for stage 0 (and the
-  // scales issued before it), make it visible, read its first step.
+  // scales issued before it), make it visible, read its first step. With
+  // in-GEMM quantization, X of stages 0..2 is loaded beside them and stages
+  // 0 and 1 are quantized here (the loop quantizes stage st + 2 in stage st).
+  static_assert(!F::kFusedQ || kFast, "in-GEMM quantization runs on whole scale groups");
   issue_scales(0);
+  if constexpr (F::kFusedQ) {
+    issue_stage(0, std::integral_constant<int, 2>{});
+    issue_stage(1, std::integral_constant<int, 2>{});
+    issue_x(0);
+    wait_vmcnt<0>();
+    quantize_x(0);
+    issue_x(1);
+    wait_vmcnt<0>();
+    quantize_x(1);
+    issue_stage(2, std::integral_constant<int, 0>{});
+  } else {
 #pragma unroll
-  for (int st = 0; st < kRing - 1; ++st) issue_stage(st, std::integral_constant<int, 2>{});
-  issue_stage(kRing - 1, std::integral_constant<int, 0>{});
-  if (kFast)
+    for (int st = 0; st < kRing - 1; ++st) issue_stage(st, std::integral_constant<int, 2>{});
+    issue_stage(kRing - 1, std::integral_constant<int, 0>{});
+  }
+  if (F::kFusedQ)
+    wait_vmcnt<kPart0>();
+  else if (kFast)
     wait_vmcnt<kDmaPerStage + kPart0>();
   else
     wait_vmcnt<0>();
@@ -731,6 +860,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     // second halves are read in stage 0's first group, as in every stage
     read_ws16(std::integral_constant<int, 0>{});
     read_xs16(std::integral_constant<int, 0>{});
+    read_xs16f(0, std::integral_constant<int, 0>{});
     read_w16(0, std::integral_constant<int, 0>{});
     read_x16(0, std::integral_constant<int, 0>{});
   } else {
@@ -750,8 +880,11 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // (issued first, see the wait).
   auto sync_and_refill = [&](auto pc, int st) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
+    // (with in-GEMM quantization the X loads of stage st + 2 went out after
+    // the second weight part of stage st + 2, and those of stage st + 1,
+    // older than the scales, are already in)
     if (kFast)
-      wait_vmcnt<kDmaPerStage>();
+      wait_vmcnt<kDmaPerStage + kLoadsX>();
     else
       wait_vmcnt<0>();
     wait_lgkmcnt0();
@@ -770,6 +903,11 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     }
     if (P == 2) issue_scales(st / kScaleGroup + 1);
     issue_stage(st + kRing, std::integral_constant<int, 0>{});
+    if constexpr (F::kFusedQ) {
+      // X of stage st + 2 (loaded at the start of this stage) must be in
+      // before it is quantized: only the loads just issued went out after it
+      wait_vmcnt<kPart0 + (P == 2 ? kScaleLoadsPerWave : 0)>();
+    }
   };
 
   auto stage = [&](auto pc, int st) __attribute__((always_inline)) {
@@ -835,32 +973,42 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     // (W0, A0): meanwhile stage st's second halves (and, at a group's first
     // stage, its second-half scale words) and the second part of stage
     // st + 2's loads
+    constexpr int PX = F::kFusedQ ? 0 : P;     // op_sel of the activation scales
+    constexpr int kXsReads = F::kFusedQ ? kXH : 0;   // per-stage scale bytes (in-GEMM quantization)
     issue_stage(st + kRing - 1, I1{});
+    issue_x(st + kRing - 1);
     read_w16(st, I1{});
     read_x16(st, I1{});
+    read_xs16f(st, I1{});
     if (P == 0) {
       read_ws16(I1{});
       read_xs16(I1{});
     }
-    mfma16_group<P, 0, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
-    interleave_hint<kHN + kXH + (P == 0 ? kHN + kXH : 0), kFast ? kDmaPerStage - kPart0 : 0, kG>();
+    mfma16_group<P, PX, 0, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    interleave_hint<kHN + kXH + kXsReads + (P == 0 ? kHN + (F::kFusedQ ? 0 : kXH) : 0),
+                    kFast ? kDmaPerStage - kPart0 + kLoadsX : 0, kG>();
     __builtin_amdgcn_sched_barrier(0);
     // (W0, A1)
-    mfma16_group<P, 0, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    mfma16_group<P, PX, 0, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
     __builtin_amdgcn_sched_barrier(0);
     sync_and_refill(pc, st);
     // (W1, A0): meanwhile stage st + 1's W0 (and at the group's last stage
-    // the next group's W0 scale words)
+    // the next group's W0 scale words); with in-GEMM quantization also the
+    // first half of stage st + 2's quantization
     read_w16(st + 1, I0{});
     if (P == 3) read_ws16(I0{});
-    mfma16_group<P, 1, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    quantize_half(st + 2, I0{});
+    mfma16_group<P, PX, 1, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
     interleave_hint<kHN + (P == 3 ? kHN : 0), kFast ? kPart0 + (P == 2 ? kScaleLoadsPerWave : 0) : 0, kG>();
     __builtin_amdgcn_sched_barrier(0);
-    // (W1, A1): meanwhile stage st + 1's A0 (and the next group's A0 scale words)
+    // (W1, A1): meanwhile stage st + 1's A0 (and the next group's A0 scale
+    // words), and the rest of stage st + 2's quantization
     read_x16(st + 1, I0{});
+    read_xs16f(st + 1, I0{});
     if (P == 3) read_xs16(I0{});
-    mfma16_group<P, 1, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
-    interleave_hint<kXH + (P == 3 ? kXH : 0), 0, kG>();
+    quantize_half(st + 2, I1{});
+    mfma16_group<P, PX, 1, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    interleave_hint<kXH + kXsReads + (P == 3 && !F::kFusedQ ? kXH : 0), 0, kG>();
     __builtin_amdgcn_sched_barrier(0);
   };
   auto run_stage = [&](auto pc, int st) __attribute__((always_inline)) {
@@ -1088,8 +1236,10 @@ hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipSt
     hipLaunchKernelGGL((gemm_kernel<C, F, kOutBf16, true, kCanStream>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
   else if (fast)
     hipLaunchKernelGGL((gemm_kernel<C, F, kOutBf16, true, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
-  else
+  else if constexpr (!F::kFusedQ)
     hipLaunchKernelGGL((gemm_kernel<C, F, kOutBf16, false, false>), dim3(p.wg), dim3(64 * C::kWaves), 0, stream, p);
+  else
+    return hipErrorInvalidValue;   // in-GEMM quantization needs K % 512 == 0 (checked by the caller)
   return hipGetLastError();
 }
 
@@ -1115,16 +1265,13 @@ hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipSt
 constexpr double kQuadRound = 0.55, kHalfRound = 0.48;
 constexpr double kQuadRoundBf16 = 0.50, kHalfRoundBf16 = 0.60;
 
+// The launch plan of every variant but in-GEMM quantization (below): big
+// tiles in whole rounds, the rest as halves or quadrants in a second launch.
 template <class F, bool kOutBf16>
-hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) {
+hipError_t launch_tiled_impl(GemmParams p, bool fast, int cus, int tiles, hipStream_t stream) {
   using Big = typename Tiles<F>::Big;
   using Quad = typename Tiles<F>::Quad;
   using Half = typename Tiles<F>::Half;
-  p.gm = Big::kBM;
-  p.gn = Big::kBN;
-  p.tiles_m = (p.M + p.gm - 1) / p.gm;
-  p.tiles_n = (p.N + p.gn - 1) / p.gn;
-  const int tiles = p.tiles_m * p.tiles_n;
   if constexpr (F::kBf16 && !F::kOutT) {
     // The bf16 product dY Wd: when 256 x 320 tiles (8 waves of 64 x 160)
     // cover Y in whole rounds and 256 x 256 tiles would leave a partial
@@ -1181,6 +1328,30 @@ hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) 
   return launch_tiles<Quad, F, kOutBf16, false>(p, fast, false, stream);
 }
 
+template <class F, bool kOutBf16>
+hipError_t launch_variant(GemmParams p, bool fast, int cus, hipStream_t stream) {
+  using Big = typename Tiles<F>::Big;
+  p.gm = Big::kBM;
+  p.gn = Big::kBN;
+  p.tiles_m = (p.M + p.gm - 1) / p.gm;
+  p.tiles_n = (p.N + p.gn - 1) / p.gn;
+  const int tiles = p.tiles_m * p.tiles_n;
+  if constexpr (F::kFusedQ) {
+    // In-GEMM quantization: one launch of 128 x 256 tiles. When they lie
+    // inside Y, one workgroup per CU streams items b, b + wg, ... (a last
+    // partial round just gives some workgroups one tile more); otherwise one
+    // workgroup per tile.
+    const bool stream_tiles = fast && p.vec_out && p.M % Big::kBM == 0 && p.N % Big::kBN == 0 && tiles > cus;
+    p.first = 0;
+    p.grid = tiles;
+    p.pieces = 1;
+    p.wg = stream_tiles ? cus : tiles;
+    return launch_tiles<Big, F, kOutBf16, true>(p, fast, stream_tiles, stream);
+  } else {
+    return launch_tiled_impl<F, kOutBf16>(p, fast, cus, tiles, stream);
+  }
+}
+
 int cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -1201,6 +1372,7 @@ hipError_t launch_gemm(int x_fmt, int r_fmt, const uint8_t* qx, const uint8_t* s
   GemmParams p;
   p.qx = qx; p.sx = sx; p.qr = qr; p.sr = sr; p.w = w; p.sw = sw;
   p.y = y; p.ldy = ldy;
+  p.ldx = 0;
   // four consecutive outputs go out as one 8-byte (bf16) or 16-byte (fp32)
   // store (transposed results go element by element, any alignment)
   const uintptr_t vec_bytes = y_bf16 ? 8 : 16;
@@ -1226,6 +1398,23 @@ hipError_t launch_gemm(int x_fmt, int r_fmt, const uint8_t* qx, const uint8_t* s
     case 80: return y_bf16 ? launch_variant<FmtW4A8, true>(p, fast, cus, stream) : launch_variant<FmtW4A8, false>(p, fast, cus, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_fused(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N,
+                             int64_t K, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
+  if (K % (kBK * kScaleGroup) != 0) return hipErrorInvalidValue;
+  GemmParams p;
+  p.qx = reinterpret_cast<const uint8_t*>(x);
+  p.sx = p.qr = p.sr = nullptr;
+  p.w = w; p.sw = sw;
+  p.y = y; p.ldy = ldy;
+  p.ldx = ldx;
+  const uintptr_t vec_bytes = y_bf16 ? 8 : 16;
+  p.vec_out = ((uintptr_t)y % vec_bytes == 0 && ldy % 4 == 0) ? 1 : 0;
+  p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
+  const int cus = cu_count();
+  return y_bf16 ? launch_variant<FmtRfqFused, true>(p, true, cus, stream)
+                : launch_variant<FmtRfqFused, false>(p, true, cus, stream);
 }
 
 }  // namespace rfq

@@ -28,6 +28,14 @@ hipError_t launch_gemm(int x_fmt, int r_fmt, const uint8_t* qx, const uint8_t* s
                        const uint8_t* sr, const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N, int64_t K,
                        void* y, bool y_bf16, int64_t ldy, hipStream_t stream, bool y_trans = false);
 
+// The RFQ GEMM that quantizes its own activation: Y = Q(X) W^T + Q(R) W^T
+// for bf16 X [M, K] (row stride ldx elements) and the MXFP4 weight, with Q(X)
+// and Q(R) formed tile by tile inside the GEMM and never written to memory.
+// K must be a multiple of 512 (hipErrorInvalidValue otherwise); 128 * ldx * 2
+// must stay below 2^32.
+hipError_t launch_gemm_fused(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint8_t* sw, int64_t M, int64_t N,
+                             int64_t K, void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
+
 // Backward-pass operand staging (csrc/backward.hip): MXFP4 codes [rows,
 // cols/2] + scales to bf16 [cols, ld_out] transposed, and a bf16 transpose
 // [rows, cols] (stride ld_in) to [cols, ld_out]; columns past `rows` are

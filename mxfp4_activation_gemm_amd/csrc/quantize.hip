@@ -45,70 +45,19 @@
 //    448 up to the 464 midpoint the nearest value is 448 anyway.
 
 #include "kernels.h"
+#include "mx_encode.h"
 
 namespace rfq {
 namespace {
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
+using namespace mx;
+
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;          // 4 waves per workgroup
 constexpr int kUnits = 4;              // 16-block units per wave
 constexpr int kBlocksPerWave = 16 * kUnits;
-
-// DPP quad permutations: lane ^ 1 and lane ^ 2 within each group of 4 lanes.
-constexpr int kQuadXor1 = 0xB1;        // quad_perm:[1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;        // quad_perm:[2,3,0,1]
-
-__device__ __forceinline__ unsigned quad_max_u32(unsigned v) {
-  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, true));
-  v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, true));
-  return v;
-}
-
-// max over 8 bf16 magnitudes, as the 15-bit magnitude pattern (monotone in
-// the value for non-NaN inputs; any pattern >= 0x7F80 is Inf or NaN).
-// (Each word is copied to a scalar before the bit cast: a bit cast applied
-// directly to an ext-vector element has been seen to read element 0.)
-__device__ __forceinline__ unsigned bf16x8_absmax_bits(u32x4_t w) {
-  const u16x2_t mask = {0x7FFF, 0x7FFF};
-  const unsigned w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
-  u16x2_t a = __builtin_bit_cast(u16x2_t, w0) & mask;
-  u16x2_t b = __builtin_bit_cast(u16x2_t, w1) & mask;
-  u16x2_t c = __builtin_bit_cast(u16x2_t, w2) & mask;
-  u16x2_t d = __builtin_bit_cast(u16x2_t, w3) & mask;
-  u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
-  return max((unsigned)m.x, (unsigned)m.y);
-}
-
-__device__ __forceinline__ float scale_operand(unsigned code) {
-  return __builtin_bit_cast(float, code << 23);  // exponent field = E8M0 code
-}
-
-// The 8 bf16 values of `w` widened to fp32 (exact): element 2j is the low
-// half of word j.
-__device__ __forceinline__ void widen_bf16x8(u32x4_t w, float* f) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f[2 * j] = __builtin_bit_cast(float, w[j] << 16);
-    f[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
-  }
-}
-
-// E2M1 codes of 8 fp32 values at scale code s (exponent field of `s`): byte j
-// holds element 2j in its low nibble and 2j+1 in its high nibble.
-__device__ __forceinline__ unsigned encode_f32x8(const float* f, float s) {
-  unsigned c = 0;
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[0], f[1], s, 0);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[2], f[3], s, 1);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[4], f[5], s, 2);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[6], f[7], s, 3);
-  return c;
-}
 
 // E4M3 codes of 8 fp32 values at E8M0 scale code `code` (not 255): byte j of
 // the 8 holds element j. Each value is first clamped to +-448 * 2^se (whose
@@ -151,15 +100,6 @@ __device__ __forceinline__ void store_part(uint8_t* q, uint32_t g, uint32_t part
     __builtin_nontemporal_store(c, reinterpret_cast<u32x2_t*>(q + (uint64_t)g * 32 + part * 8));
   else
     __builtin_nontemporal_store(c.x, reinterpret_cast<unsigned*>(q + (uint64_t)g * 16 + part * 4));
-}
-
-// r[2J], r[2J+1] = x[2J], x[2J+1] minus their decoded codes (byte J of
-// `codes`), in fp32.
-template <int J>
-__device__ __forceinline__ void residual_pair(const float* x, unsigned codes, float s, float* r) {
-  const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, s, J);
-  r[2 * J] = x[2 * J] - d.x;
-  r[2 * J + 1] = x[2 * J + 1] - d.y;
 }
 
 // One butterfly pass across lanes: this lane's element pairs with the same

@@ -36,11 +36,11 @@ def declared_functions():
 
 def test_header_declarations_are_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
-    assert lib.rfq_abi_version() == 6
+    assert lib.rfq_abi_version() == 7
 
 
 def status_name(st):
@@ -218,3 +218,18 @@ def test_linear_noalloc_validation(lib):
     assert na(M=12400, K=5120, ldx=5120) == "RFQ_ERR_WORKSPACE_TOO_SMALL"
     assert "allocation-free" in lib.rfq_last_error_detail().decode()
     assert na(M=0, x=None, w=None, sw=None, y=None) == "RFQ_OK"
+
+
+def test_linear_fused_validation(lib):
+    f = lib.rfq_linear_fused
+
+    def lf(x=FAKE, dt=0, M=8, K=512, ldx=512, w=FAKE, sw=FAKE, N=8, y=FAKE, yd=1, ldy=8):
+        return status_name(f(x, dt, M, K, ldx, w, sw, N, y, yd, ldy, None))
+    assert lf(dt=1) == "RFQ_ERR_UNSUPPORTED_DTYPE"                # fp32 X is not taken
+    assert lf(K=256, ldx=256) == "RFQ_ERR_INVALID_SHAPE"          # K must be a multiple of 512
+    assert lf(K=96, ldx=96) == "RFQ_ERR_INVALID_SHAPE"
+    assert lf(ldx=1 << 24) == "RFQ_ERR_INVALID_STRIDE"
+    assert lf(x=None) == "RFQ_ERR_NULL_POINTER"
+    assert lf(ldy=4) == "RFQ_ERR_INVALID_STRIDE"
+    assert lf(x=FAKE + 2) == "RFQ_ERR_MISALIGNED"
+    assert lf(M=0, x=None, w=None, sw=None, y=None) == "RFQ_OK"
