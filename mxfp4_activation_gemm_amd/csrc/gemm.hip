@@ -454,6 +454,20 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   const int ngroups = (nstages + kScaleGroup - 1) / kScaleGroup;
   const int total_stages = ntiles * nstages;
 
+  // Byte offset of stage st's ring slot (slot st mod 3). The K loop advances
+  // by a scale group (4 stages, 1 mod 3) per iteration, so instead of
+  // reducing st mod 3 at every use it keeps the offsets of the slots of
+  // stages st0, st0 + 1 and st0 + 2 (st0 the iteration's first stage) and
+  // rotates them once per iteration; every use names its stage as st0 plus a
+  // distance known at compile time. (Same-box A/B against st mod 3 at every
+  // use: 283.7 against 284.8 us on the 4096 x 5120 x 13824 layer, 39.8
+  // against 40.7 us on 2048 x 4096 x 4096; Y bit-identical.)
+  int loop_st0 = 0;
+  uint32_t rot[3] = {0u, (uint32_t)kStageBytes, 2u * kStageBytes};
+  auto slot_off = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    return rot[(st - loop_st0) % kRing];
+  };
+
   // Buffer descriptors of the tile being fetched (rows past the tensor read
   // as zero), one per activation sub-tile: an E4M3 term's second sub-tile
   // starts 32 bytes (two chunks) into the row, so the same offsets fetch it.
@@ -538,7 +552,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   constexpr int kPart0 = (kDmaPerStage + 1) / 2;
   auto issue_stage = [&](int st, auto part_c) __attribute__((always_inline)) {
     constexpr int part = decltype(part_c)::value;   // 0: first kPart0 loads, 1: the rest, 2: all
-    uint8_t* buf = ring + (st % kRing) * kStageBytes;
+    uint8_t* buf = ring + slot_off(st);
     const int kst = st - load_base;
     const bool past_end = st >= total_stages;
     const uint32_t kst_s = past_end ? 0u : (uint32_t)kst;   // kFast: stage in the scalar offset
@@ -660,7 +674,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   auto quantize_units = [&](int st, auto u0_c, auto u1_c) __attribute__((always_inline)) {
     if constexpr (F::kFusedQ) {
       constexpr int u0 = decltype(u0_c)::value, u1 = decltype(u1_c)::value;
-      uint8_t* slot = ring + (st % kRing) * kStageBytes;
+      uint8_t* slot = ring + slot_off(st);
       const uint32_t blk = (lane >> 2) & 3, part = lane & 3;
 #pragma unroll
       for (int u = u0; u < u1; ++u) {
@@ -701,7 +715,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     // precomputed address per ring slot and fragment through the loop.)
     uint32_t off = rd_off[s];
     asm volatile("" : "+v"(off));
-    const uint8_t* buf = ring + (st % kRing) * kStageBytes + off;
+    const uint8_t* buf = ring + slot_off(st) + off;
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
       const uint8_t* src = buf + (a_row0 + 32 * i) * kRowBytes;
@@ -749,7 +763,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     constexpr int h = decltype(h_c)::value;
     uint32_t off = rd16;
     asm volatile("" : "+v"(off));
-    const uint8_t* buf = ring + (st % kRing) * kStageBytes + kSubA * kTileBytesA + off;
+    const uint8_t* buf = ring + slot_off(st) + kSubA * kTileBytesA + off;
 #pragma unroll
     for (int n = 0; n < kHN; ++n) wf[h][n] = read_frag(buf + (b_row0 + 16 * (h * kHN + n)) * kRowBytes);
   };
@@ -757,7 +771,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     constexpr int h = decltype(h_c)::value;
     uint32_t off = rd16;
     asm volatile("" : "+v"(off));
-    const uint8_t* buf = ring + (st % kRing) * kStageBytes + off;
+    const uint8_t* buf = ring + slot_off(st) + off;
 #pragma unroll
     for (int m = 0; m < kHM; ++m)
 #pragma unroll
@@ -794,7 +808,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   auto read_xs16f = [&](int st, auto h_c) __attribute__((always_inline)) {
     constexpr int h = decltype(h_c)::value;
     if constexpr (F::kFusedQ) {
-      const uint8_t* sc = ring + (st % kRing) * kStageBytes + C::kStageScaleOff + (lane >> 4);
+      const uint8_t* sc = ring + slot_off(st) + C::kStageScaleOff + (lane >> 4);
 #pragma unroll
       for (int m = 0; m < kHM; ++m) {
         const uint32_t row = a_row0 + 16 * (h * kHM + m) + (lane & 15);
@@ -964,16 +978,30 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // One stage on the 16 x 16 x 128 path: four MFMA groups, the barrier
   // after the second; the reads beside each group are the halves freed by
   // the groups before it (see the register note above).
+  // One group of 16 x 16 x 128 MFMAs, (weight half HW, activation half HX),
+  // with the LDS reads (kReads) and loads (kVmem) issued before it in
+  // program order spread among its MFMAs. (The scheduler places the two
+  // MFMAs into one accumulator next to each other in some groups; fencing
+  // the X terms from the R terms so that they stay kHM x kHN apart measured
+  // 1% slower, so the hardware's result forwarding covers that.)
+  auto group16 = [&](auto pc, auto hw_c, auto hx_c, auto reads_c, auto vmem_c) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    constexpr int PX = F::kFusedQ ? 0 : P;
+    constexpr int HW = decltype(hw_c)::value, HX = decltype(hx_c)::value;
+    constexpr int kReads = decltype(reads_c)::value, kVmem = decltype(vmem_c)::value;
+    constexpr int kG = kHM * kHN * F::kTerms;
+    mfma16_group<P, PX, HW, HX, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    if constexpr (kReads + kVmem > 0) interleave_hint<kReads, kVmem, kG>();
+  };
+
   auto stage16 = [&](auto pc, int st) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    constexpr int kG = kHM * kHN * F::kTerms;   // MFMAs per group
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     __builtin_amdgcn_sched_barrier(0);
     // (W0, A0): meanwhile stage st's second halves (and, at a group's first
     // stage, its second-half scale words) and the second part of stage
     // st + 2's loads
-    constexpr int PX = F::kFusedQ ? 0 : P;     // op_sel of the activation scales
     constexpr int kXsReads = F::kFusedQ ? kXH : 0;   // per-stage scale bytes (in-GEMM quantization)
     issue_stage(st + kRing - 1, I1{});
     issue_x(st + kRing - 1);
@@ -984,12 +1012,11 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       read_ws16(I1{});
       read_xs16(I1{});
     }
-    mfma16_group<P, PX, 0, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
-    interleave_hint<kHN + kXH + kXsReads + (P == 0 ? kHN + (F::kFusedQ ? 0 : kXH) : 0),
-                    kFast ? kDmaPerStage - kPart0 + kLoadsX : 0, kG>();
+    group16(pc, I0{}, I0{}, std::integral_constant<int, kHN + kXH + kXsReads + (P == 0 ? kHN + (F::kFusedQ ? 0 : kXH) : 0)>{},
+            std::integral_constant<int, kFast ? kDmaPerStage - kPart0 + kLoadsX : 0>{});
     __builtin_amdgcn_sched_barrier(0);
     // (W0, A1)
-    mfma16_group<P, PX, 0, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    group16(pc, I0{}, I1{}, I0{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
     sync_and_refill(pc, st);
     // (W1, A0): meanwhile stage st + 1's W0 (and at the group's last stage
@@ -998,8 +1025,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     read_w16(st + 1, I0{});
     if (P == 3) read_ws16(I0{});
     quantize_half(st + 2, I0{});
-    mfma16_group<P, PX, 1, 0, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
-    interleave_hint<kHN + (P == 3 ? kHN : 0), kFast ? kPart0 + (P == 2 ? kScaleLoadsPerWave : 0) : 0, kG>();
+    group16(pc, I1{}, I0{}, std::integral_constant<int, kHN + (P == 3 ? kHN : 0)>{},
+            std::integral_constant<int, kFast ? kPart0 + (P == 2 ? kScaleLoadsPerWave : 0) : 0>{});
     __builtin_amdgcn_sched_barrier(0);
     // (W1, A1): meanwhile stage st + 1's A0 (and the next group's A0 scale
     // words), and the rest of stage st + 2's quantization
@@ -1007,8 +1034,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     read_xs16f(st + 1, I0{});
     if (P == 3) read_xs16(I0{});
     quantize_half(st + 2, I1{});
-    mfma16_group<P, PX, 1, 1, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
-    interleave_hint<kXH + kXsReads + (P == 3 && !F::kFusedQ ? kXH : 0), 0, kG>();
+    group16(pc, I1{}, I1{}, std::integral_constant<int, kXH + kXsReads + (P == 3 && !F::kFusedQ ? kXH : 0)>{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
   };
   auto run_stage = [&](auto pc, int st) __attribute__((always_inline)) {
@@ -1208,6 +1234,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // register allocator needs to fit this loop without spills)
   int comp_base = 0, comp_tile = 0;
   for (int st = 0; st < total_stages; st += kScaleGroup) {
+    loop_st0 = st;
     run_stage(std::integral_constant<int, 0>{}, st);
     if (st + 1 < total_stages) run_stage(std::integral_constant<int, 1>{}, st + 1);
     if (st + 2 < total_stages) run_stage(std::integral_constant<int, 2>{}, st + 2);
@@ -1222,6 +1249,10 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       const GemmParams q = fresh_params();
       tile_origin(q, (int)blockIdx.x + comp_tile * q.wg, cm0, cn0);
     }
+    const uint32_t r0 = rot[0];
+    rot[0] = rot[1];
+    rot[1] = rot[2];
+    rot[2] = r0;
   }
   if (kStream)
     store_full_tile(cm0, cn0);
