@@ -120,9 +120,12 @@ rfq_status_t rfq_residual_quantize(const void* x, int x_dtype, int64_t M, int64_
  * applied to every 32-element block along K, i.e. to every MX block; H H^T =
  * 32 I, so with X H on the activation side and W H / 32 on the weight side
  * rfq_gemm_w4a4 returns (X H)(W H / 32)^T = X W^T up to quantization.
- * X H is formed in fp32 by five butterfly passes of spans 1, 2, 4, 8, 16,
- * each taking (a, b) at block positions (i, i + span), i & span == 0, to
- * (a + b, a - b); the codes are decided on those fp32 values.
+ * Each value of X H (of W H / 32) is the exact block sum rounded once to
+ * fp32, ties to even, a zero sum being +0; the codes are decided on those
+ * fp32 values. The sums are exact when a block's terms lie within 53 bits
+ * of each other (nonzero bf16 values within 40 binades, fp32 within 24);
+ * in wider blocks an fp64 partial sum can round, and the result can then
+ * differ from the exact one (no bound is claimed there).
  *
  * rfq_rotate_residual_quantize - the RFQ encoding of X H: Q(X H), then
  *   R = X H - deq(Q(X H)) (exact in fp32), then Q(R). Arguments, layouts and

@@ -29,13 +29,18 @@
 //  * rotation before quantization ("大模型量化中的双线性尾部问题与QuaRot正交旋转
 //    解决方案" §3, QuaRot: an orthogonal +-1 matrix applied online to the
 //    activation and folded into the weight): each 32-block is multiplied by
-//    the unnormalised 32 x 32 Sylvester Hadamard matrix H in fp32, by five
+//    the unnormalised 32 x 32 Sylvester Hadamard matrix H, and each output,
+//    the exact sum of the block's 32 values with signs (over 32 for the
+//    weight), is rounded once to fp32. The sums are formed in fp64 by five
 //    butterfly passes of spans 1, 2, 4 (inside a lane) and 8, 16 (across the
 //    block's four lanes, DPP), each taking (a, b) at (i, i + span) to
-//    (a + b, a - b). Activations quantize X H; weights W H / 32 (an exact
-//    power of two), so the GEMM returns X W^T unchanged. Codes are decided
-//    on the rotated fp32 values; the residual stays exact (|R| is at most
-//    half an E2M1 step, so R = v - deq(v) loses no bits in fp32);
+//    (a + b, a - b); they are exact whenever the block's terms span at most
+//    53 bits (a bf16 block whose nonzero values span at most 40 binades, an
+//    fp32 one 24), and then the one fp64 -> fp32 conversion is the only
+//    rounding. Activations quantize X H; weights W H / 32 (an exact power of
+//    two), so the GEMM returns X W^T unchanged. Codes are decided on the
+//    rotated fp32 values; the residual stays exact (|R| is at most half an
+//    E2M1 step, so R = v - deq(v) loses no bits in fp32);
 //  * MXFP8 output ("Activation Outliers Matter", Abstract and §1 study MXFP8
 //    beside MXFP4; elements per OCP MX v1.0): E4M3 codes, one byte per
 //    element, with se = max(floor(log2 amax) - 8, -127), either for X itself
@@ -102,35 +107,47 @@ __device__ __forceinline__ void store_part(uint8_t* q, uint32_t g, uint32_t part
     __builtin_nontemporal_store(c.x, reinterpret_cast<unsigned*>(q + (uint64_t)g * 16 + part * 4));
 }
 
-// One butterfly pass across lanes: this lane's element pairs with the same
-// element of lane (lane ^ kXor) in its quad; the lane with the span bit clear
-// keeps a + b, the other a - b (a = the clear lane's value).
-// (o - a is formed as (-a) + o: negation is exact, so the result is the same
-// IEEE sum, and the partner's value can feed the add through DPP directly.)
+// One fp64 butterfly pass across lanes: this lane's element pairs with the
+// same element of lane (lane ^ kXor) in its quad; the lane with the span bit
+// clear keeps a + b, the other a - b (a = the clear lane's value). The
+// partner's value comes over as two 32-bit DPP moves. (a - b is formed as
+// (-b) + a: negation is exact, so it is the same IEEE sum.)
 template <int kDpp>
-__device__ __forceinline__ void butterfly_across(float* v, bool upper) {
-  const unsigned flip = upper ? 0x80000000u : 0u;
+__device__ __forceinline__ void butterfly_across_f64(double* v, bool upper) {
+  const uint64_t flip = upper ? 0x8000000000000000ull : 0ull;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float o = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[j]), kDpp, 0xF, 0xF, true));
-    v[j] = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, v[j]) ^ flip) + o;
+    const uint64_t u = __builtin_bit_cast(uint64_t, v[j]);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, kDpp, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), kDpp, 0xF, 0xF, true);
+    const double o = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    v[j] = __builtin_bit_cast(double, u ^ flip) + o;
   }
 }
 
 // Walsh-Hadamard transform of the 32-block held by a quad of lanes (lane part
-// p holds elements 8 p .. 8 p + 7), unnormalised, in the pass order above.
-__device__ __forceinline__ void hadamard32(float* v, unsigned part) {
+// p holds elements 8 p .. 8 p + 7), unnormalised (times 1/32 with div32, an
+// exact scaling in fp64): the sums in fp64 by the passes above, then one
+// rounding of each to fp32. A sum that is exactly zero comes out as +0,
+// whatever the signs of the zeros summed (IEEE gives -0 + -0 = -0, so the
+// passes alone would keep -0 for a block of negative zeros).
+__device__ __forceinline__ void hadamard32(float* f, unsigned part, bool div32) {
+  double v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (double)f[j];
 #pragma unroll
   for (int span = 1; span < 8; span *= 2)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (!(j & span)) {
-        const float a = v[j], b = v[j + span];
+        const double a = v[j], b = v[j + span];
         v[j] = a + b;
         v[j + span] = a - b;
       }
-  butterfly_across<kQuadXor1>(v, part & 1);   // span 8
-  butterfly_across<kQuadXor2>(v, part & 2);   // span 16
+  butterfly_across_f64<kQuadXor1>(v, part & 1);   // span 8
+  butterfly_across_f64<kQuadXor2>(v, part & 2);   // span 16
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (float)((div32 ? v[j] * 0.03125 : v[j]) + 0.0);   // + 0: an exact zero is +0
 }
 
 // max over 8 fp32 magnitudes as a bit pattern (monotone in the value for
@@ -207,13 +224,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
       } else {
         widen_bf16x8(w[u][0], xf);
       }
-      if (kRotate != 0) {
-        hadamard32(xf, part);
-        if (kRotate == 2) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xf[j] *= 0.03125f;   // 1/32, exact
-        }
-      }
+      if (kRotate != 0) hadamard32(xf, part, kRotate == 2);
       e = quad_max_u32(f32x8_absmax_bits(xf)) >> 23;
     }
     const bool nonfinite = e == 255;

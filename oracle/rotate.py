@@ -15,56 +15,113 @@ per-token INT4 scheme; MX quantization scales per 32-element block):
 * the activation side quantizes X H, the weight side W H / 32, so that
   (X H)(W H / 32)^T = X (H H^T / 32) W^T = X W^T, because H H^T = 32 I; the
   1/32 is a power of two and costs no rounding;
-* X H is formed in float32 by the fast transform: five butterfly passes with
-  spans 1, 2, 4, 8, 16, each replacing (a, b) at positions (i, i + span),
-  i & span == 0, by (a + b, a - b). The quantization codes are decided on these
-  float32 values, in the precision the kernel computes them, so the pass order
-  is part of the definition. Everything after the rotation is the plain
-  oracle (``quantize_mxfp4`` / ``residual_quantize``) on those values; the
-  residual is exact there (see ``residual_quantize``).
+* each rotated value is the exact sum (x H)[i] = sum_j H[j, i] x[j] over its
+  block (divided by 32 on the weight side), rounded once to the nearest
+  float32, ties to even, an exact zero being +0 (the sum of zeros has no
+  sign of its own): a definition with no summation order in it. The
+  quantization codes are decided on these float32 values (the precision the
+  quantize pass computes in), then everything is the plain oracle
+  (``quantize_mxfp4`` / ``residual_quantize``); the residual is exact there.
+
+Computing the exact sum: when every term is a multiple of 2^L and the sum of
+magnitudes is below 2^U with U - L <= 53, every partial sum in any order is
+exact in float64, so a float64 matrix product gives the exact value (for
+bfloat16 inputs this holds whenever the block's nonzero values span at most
+40 binades, for float32 ones 24). Blocks outside that are summed as exact
+rationals and rounded to float32 directly.
 """
+
+from fractions import Fraction
 
 import numpy as np
 
 from .formats import BLOCK
 from .quantize import quantize_mxfp4, residual_quantize
 
-_SPANS = (1, 2, 4, 8, 16)
-_WEIGHT_SCALE = np.float32(1.0 / BLOCK)      # 2^-5, exact
+# Sylvester order: H[i, j] = (-1)^popcount(i & j)
+_H = np.array([[-1.0 if bin(i & j).count("1") % 2 else 1.0 for j in range(BLOCK)] for i in range(BLOCK)])
 
 
-def hadamard32_f32(x):
-    """Per-32-block Walsh-Hadamard transform along the last axis, in float32.
+def _lsb_exponent(v):
+    """Exponent of the lowest set bit of each finite nonzero float64 value
+    (v = m 2^L with m odd); +inf where v == 0."""
+    bits = np.abs(v).view(np.uint64)
+    exp_field = ((bits >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64)
+    mant = bits & np.uint64((1 << 52) - 1)
+    mant = np.where(exp_field > 0, mant | np.uint64(1 << 52), mant)
+    low = mant & (~mant + np.uint64(1))                     # lowest set bit of the integer significand
+    _, e = np.frexp(low.astype(np.float64))                 # low = 2^(e - 1)
+    unbiased = np.where(exp_field > 0, exp_field - 1075, -1074)   # value = mant * 2^unbiased
+    return np.where(v == 0, np.inf, unbiased + e - 1)
 
-    ``x`` [..., K] (K a multiple of 32) is converted to float32 and each block
-    of 32 is transformed by the butterfly passes listed in the module
-    docstring. Returns float32 of the same shape.
-    """
-    v = np.array(x, dtype=np.float32, copy=True)
+
+def fraction_to_f32(q):
+    """The float32 nearest the rational q (ties to even), as a float64;
+    +-inf past the largest float32 (rounding as IEEE does)."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^(e-1) <= a < 2^(e+1)
+    if Fraction(2) ** e <= a:
+        e += 1
+    # now 2^(e-1) <= a < 2^e; float32 keeps 24 bits, or fewer below 2^-126
+    ulp_exp = max(e - 24, -149)
+    n = a / Fraction(2) ** ulp_exp
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    val = lo * 2.0 ** ulp_exp
+    if val >= 2.0 ** 128:
+        return sign * np.inf
+    return sign * val
+
+
+def hadamard32_rounded(x, divide_by_32=False):
+    """Per-32-block Walsh-Hadamard transform along the last axis: each output
+    the exact block sum (times 1/32 if ``divide_by_32``) rounded once to
+    float32. ``x`` [..., K] holds finite or non-finite float64 values; a
+    block with a NaN or an infinity gives NaN/inf outputs as float32 sums
+    would. Returns float32 of the same shape."""
+    v = np.asarray(x, dtype=np.float64)
     if v.shape[-1] % BLOCK:
         raise ValueError("the last axis must be a multiple of 32")
     lead = v.shape[:-1]
-    b = v.reshape(*lead, v.shape[-1] // BLOCK, BLOCK)
-    for span in _SPANS:
-        # positions i with bit `span` clear pair with i + span
-        lo = np.array([i for i in range(BLOCK) if not i & span])
-        a, c = b[..., lo].copy(), b[..., lo + span].copy()
-        b[..., lo] = a + c
-        b[..., lo + span] = a - c
-    return b.reshape(v.shape)
+    b = v.reshape(-1, BLOCK)
+    with np.errstate(invalid="ignore", over="ignore"):
+        prod = b @ _H                                         # H is symmetric: row block times H
+    if divide_by_32:
+        prod = prod / 32.0                                    # exact: a power of two
+    prod = prod + 0.0                                         # an exact zero is +0
+    finite = np.isfinite(b).all(axis=1)
+    mag = np.abs(np.where(np.isfinite(b), b, 0.0)).sum(axis=1)
+    L = _lsb_exponent(np.where(np.isfinite(b), b, 0.0)).min(axis=1)
+    with np.errstate(divide="ignore"):
+        U = np.floor(np.log2(np.where(mag > 0, mag, 1.0))) + 2   # sum of magnitudes < 2^U, with margin
+    exact = ~finite | (mag == 0) | (U - L <= 53)
+    out = prod.astype(np.float32)                             # one rounding of an exact value
+    for r in np.nonzero(~exact)[0]:
+        terms = [Fraction(float(t)) for t in b[r]]
+        for i in range(BLOCK):
+            q = sum(terms[j] if _H[j, i] > 0 else -terms[j] for j in range(BLOCK))
+            if divide_by_32:
+                q /= 32
+            out[r, i] = np.float32(fraction_to_f32(q))
+    return out.reshape(*lead, v.shape[-1])
 
 
 def rotate_residual_quantize(x):
     """RFQ encoding of the rotated activation X H (``x`` [M, K], values exactly
     representable in float32, e.g. decoded bfloat16): returns (qx, sx, qr, sr)
     as ``residual_quantize`` does."""
-    v = hadamard32_f32(x).astype(np.float64)
+    v = hadamard32_rounded(x).astype(np.float64)
     return residual_quantize(v)
 
 
 def rotate_quantize_weight(w):
     """MXFP4 codes and scales of the rotated weight W H / 32 (``w`` [N, K])."""
-    v = (hadamard32_f32(w) * _WEIGHT_SCALE).astype(np.float64)
+    v = hadamard32_rounded(w, divide_by_32=True).astype(np.float64)
     return quantize_mxfp4(v)
 
 

@@ -113,6 +113,52 @@ def test_rotated_activation_and_weight_bit_exact(dtype):
     check_mx(got_w, oracle.rotate_quantize_weight(w64), f"rotated W {dtype}")
 
 
+H32 = np.array([[-1.0 if bin(i & j).count("1") % 2 else 1.0 for j in range(32)] for i in range(32)])
+
+
+def near_tie_blocks(rng, rows, K, weight=False):
+    """Blocks whose rotated values sit within about an ulp of E2M1 rounding
+    ties: V holds a 4 (which fixes the scale) and tie values (0.25, 0.75, ...,
+    5) times 2^se, D perturbs them by up to 2^-21, and the input is
+    (V + D) H / 32 (or (V + D) H for a weight, whose side divides by 32)
+    rounded to float32, which leaves every value with a full significand.
+    Rounding the rotated sums along the way (a float32 butterfly) moves
+    thousands of them across a tie; only the exact sum rounded once lands
+    where the oracle does."""
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    nb = rows * K // 32
+    V = rng.choice(ties, size=(nb, 32)) * rng.choice([-1, 1], size=(nb, 32))
+    V[:, 0] = 4.0
+    se = rng.integers(-10, 10, size=(nb, 1)).astype(np.float64)
+    D = rng.uniform(-1, 1, size=(nb, 32)) * 2.0 ** -21
+    X = ((V + D) @ H32) * np.exp2(se) / (1.0 if weight else 32.0)
+    return X.astype(np.float32).reshape(rows, K)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rotation_is_the_exact_sum_rounded_once(dtype):
+    """Every rotated value must be the exact block sum rounded once to
+    float32: on near-tie blocks the codes of the order-free oracle differ in
+    thousands of bytes from those a float32 butterfly gives (checked on the
+    CPU when this test was written), so only an exact-then-round kernel
+    passes. The sums fit float64's 53 bits here, the kernel's exactness
+    condition."""
+    rng = np.random.default_rng(45 if dtype == "fp32" else 46)
+    M, N, K = 96, 64, 512
+    x, w = near_tie_blocks(rng, M, K), near_tie_blocks(rng, N, K, weight=True)
+    if dtype == "fp32":
+        xd, wd, x64, w64 = dev_f32(x), dev_f32(w), x.astype(np.float64), w.astype(np.float64)
+    else:
+        xb, wb = workloads.f32_to_bf16_bits(x), workloads.f32_to_bf16_bits(w)
+        xd, wd, x64, w64 = dev_bf16(xb), dev_bf16(wb), oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb)
+    log(f"[rotate] near-tie blocks, {dtype}")
+    got_x = rfq.rotate_residual_quantize(xd)
+    got_w = rfq.rotate_quantize_weight(wd)
+    torch.cuda.synchronize()
+    check_rfq(got_x, oracle.rotate_residual_quantize(x64), f"rotated X {dtype}")
+    check_mx(got_w, oracle.rotate_quantize_weight(w64), f"rotated W {dtype}")
+
+
 @pytest.mark.parametrize("M,N,K", [(130, 200, 512), (64, 96, 160)])
 def test_rotated_layer_every_output(M, N, K):
     """Q(XH), Q(R) and Q(WH/32) from the GPU into the unchanged W4A4 GEMM;

@@ -1,7 +1,10 @@
 """Pins of the block-Hadamard rotation in the oracle ("大模型量化中的双线性尾部问题与
 QuaRot正交旋转解决方案", §3: an orthogonal +-1 rotation before quantization,
-folded into the weight). Against the Sylvester matrix from scipy, closed-form
+folded into the weight). Against the Sylvester matrix from scipy, exact
+rational sums rounded to float32 by NumPy's own float32 conversion, closed-form
 identities of H, and a layer built so that every quantization is exact."""
+from fractions import Fraction
+
 import numpy as np
 import scipy.linalg
 
@@ -12,27 +15,94 @@ H32 = scipy.linalg.hadamard(32).astype(np.float64)     # Sylvester order, H[i,j]
 
 def test_transform_is_the_sylvester_matrix_on_exact_inputs():
     rng = np.random.default_rng(0)
-    x = rng.integers(-8, 9, size=(7, 96)).astype(np.float64)     # every partial sum exact in float32
-    got = oracle.hadamard32_f32(x).astype(np.float64)
+    x = rng.integers(-8, 9, size=(7, 96)).astype(np.float64)     # every sum exact in float32
+    got = oracle.hadamard32_rounded(x).astype(np.float64)
     want = (x.reshape(7, 3, 32) @ H32).reshape(7, 96)           # H symmetric: row blocks times H
     assert np.array_equal(got, want)
 
 
-def test_transform_rounding_on_general_inputs():
+def exact_rounded(block, div32=False):
+    """Each output of one 32-block: the exact rational sum with the Sylvester
+    signs, rounded to float32 as a Python float is: NumPy's float32 cast of a
+    float64 is a single rounding when the float64 holds the sum exactly,
+    which the sums here are built to satisfy (checked)."""
+    out = []
+    for i in range(32):
+        q = sum(Fraction(float(block[j])) * int(H32[j, i]) for j in range(32))
+        if div32:
+            q /= 32
+        assert Fraction(float(q)) == q          # exact in float64
+        out.append(np.float32(float(q)))
+    return np.array(out, dtype=np.float32)
+
+
+def test_each_output_is_the_exact_sum_rounded_once():
+    """float32 inputs with 24-bit significands over a few binades: each output
+    must be the exact sum rounded once, whatever order would have summed it.
+    On these blocks a float32 butterfly (five roundings) gets some outputs
+    wrong, so an oracle that summed in some float32 order would fail here."""
     rng = np.random.default_rng(1)
-    x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 256)))).astype(np.float32)
-    got = oracle.hadamard32_f32(x).astype(np.float64)
-    want = (x.astype(np.float64).reshape(64, 8, 32) @ H32).reshape(64, 256)
-    scale = (np.abs(x.astype(np.float64)).reshape(64, 8, 32).sum(axis=2, keepdims=True) * np.ones((1, 1, 32))).reshape(64, 256)
-    # five float32 roundings per output, each at most half an ulp of a partial sum bounded by sum |x|
-    assert (np.abs(got - want) <= 5 * 2.0 ** -24 * scale).all()
+    x = (rng.uniform(1, 2, (40, 64)) * np.exp2(rng.integers(0, 12, (40, 64)))
+         * rng.choice([-1, 1], (40, 64))).astype(np.float32).astype(np.float64)
+    got = oracle.hadamard32_rounded(x)
+    for w in (False, True):
+        got = oracle.hadamard32_rounded(x, divide_by_32=w)
+        for r in range(40):
+            for b in range(2):
+                assert np.array_equal(got[r, 32 * b:32 * b + 32], exact_rounded(x[r, 32 * b:32 * b + 32], w))
+    # the float32 butterfly, for contrast: it differs from the exact rounding somewhere
+    v = x.astype(np.float32).reshape(-1, 32).copy()
+    for span in (1, 2, 4, 8, 16):
+        lo = np.array([i for i in range(32) if not i & span])
+        a, c = v[:, lo].copy(), v[:, lo + span].copy()
+        v[:, lo], v[:, lo + span] = a + c, a - c
+    assert not np.array_equal(v.reshape(x.shape), oracle.hadamard32_rounded(x))
+
+
+def test_wide_blocks_take_the_rational_path():
+    """Blocks whose terms span more than float64's 53 bits (a huge value, a
+    tiny one and cancellation): the exact sum is formed as a rational and
+    rounded to float32 directly (checked against an independent rounding of
+    the same rationals: nearest of the float32 neighbours, ties to even)."""
+    x = np.zeros((3, 32))
+    x[0, 0], x[0, 1], x[0, 2] = 2.0 ** 100, -(2.0 ** 100), 1.5 * 2.0 ** -60
+    x[1, :] = 1.0
+    x[1, 5] = 2.0 ** 70
+    x[1, 6] = 2.0 ** -20
+    x[2, 0], x[2, 3] = 3.0 * 2.0 ** 80, 2.0 ** -80
+    got = oracle.hadamard32_rounded(x)
+    for r in range(3):
+        for i in range(32):
+            q = sum(Fraction(float(x[r, j])) * int(H32[j, i]) for j in range(32))
+            f = np.float32(float(q))            # float64 first, then float32: may round twice
+            cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+            dist = [abs(Fraction(float(c)) - q) for c in cands]
+            best = min(dist)
+            winners = [c for c, d in zip(cands, dist) if d == best]
+            want = winners[0] if len(winners) == 1 else [c for c in winners
+                                                        if not np.frombuffer(c.tobytes(), np.uint32)[0] & 1][0]
+            assert got[r, i] == want, (r, i)
+    # the cancellation survives: output 0 of row 0 is the small term, not 0
+    assert got[0, 0] == np.float32(1.5 * 2.0 ** -60)
+
+
+def test_fraction_to_f32_landmarks():
+    assert oracle.fraction_to_f32(Fraction(1, 3)) == float(np.float32(1 / 3))
+    assert oracle.fraction_to_f32(Fraction(2) ** -149) == 2.0 ** -149            # smallest subnormal
+    assert oracle.fraction_to_f32(Fraction(2) ** -150) == 0.0                     # tie to even (0)
+    assert oracle.fraction_to_f32(Fraction(3) * Fraction(2) ** -151) == 2.0 ** -149
+    big = Fraction(2) ** 128 - Fraction(2) ** 103                                 # the overflow midpoint
+    assert oracle.fraction_to_f32(big) == float("inf")
+    assert oracle.fraction_to_f32(big - 1) == float(np.finfo(np.float32).max)
+    assert oracle.fraction_to_f32(-Fraction(1) - Fraction(2) ** -24) == -1.0     # tie to even
+    assert oracle.fraction_to_f32(Fraction(1) + Fraction(3) * Fraction(2) ** -25) == 1.0 + 2.0 ** -23
 
 
 def test_twice_is_32_times_identity_and_energy_scales_by_32():
     rng = np.random.default_rng(2)
     x = rng.integers(-20, 21, size=(5, 64)).astype(np.float64)
-    once = oracle.hadamard32_f32(x).astype(np.float64)
-    twice = oracle.hadamard32_f32(once).astype(np.float64)
+    once = oracle.hadamard32_rounded(x).astype(np.float64)
+    twice = oracle.hadamard32_rounded(once).astype(np.float64)
     assert np.array_equal(twice, 32 * x)
     assert np.array_equal((once ** 2).reshape(5, 2, 32).sum(axis=2), 32 * (x ** 2).reshape(5, 2, 32).sum(axis=2))
 
@@ -40,7 +110,7 @@ def test_twice_is_32_times_identity_and_energy_scales_by_32():
 def test_a_spike_spreads_evenly_over_its_block_only():
     x = np.zeros((1, 64))
     x[0, 37] = 100.0
-    v = oracle.hadamard32_f32(x).astype(np.float64)
+    v = oracle.hadamard32_rounded(x).astype(np.float64)
     assert (v[0, :32] == 0).all()
     assert (np.abs(v[0, 32:]) == 100.0).all()
     assert np.array_equal(np.sign(v[0, 32:]), H32[37 - 32])      # the spike's row of H
@@ -78,7 +148,7 @@ def test_weight_side_carries_the_one_over_32():
     rng = np.random.default_rng(4)
     w = rng.normal(0, 0.02, (3, 64)).astype(np.float32).astype(np.float64)
     wq, sw = oracle.rotate_quantize_weight(w)
-    q0, s0 = oracle.quantize_mxfp4(oracle.hadamard32_f32(w).astype(np.float64))
+    q0, s0 = oracle.quantize_mxfp4(oracle.hadamard32_rounded(w).astype(np.float64))
     assert np.array_equal(wq, q0)                     # same codes, scales 2^-5 apart
     assert np.array_equal(sw.astype(int), s0.astype(int) - 5)
 
@@ -89,3 +159,13 @@ def test_nonfinite_input_poisons_only_its_block():
     qx, sx, qr, sr = oracle.rotate_residual_quantize(x)
     assert sx[0, 0] == 255 and sr[0, 0] == 255 and (qx[0, :32] == 0).all()
     assert sx[0, 1] != 255
+
+
+def test_an_exact_zero_sum_is_positive_zero():
+    x = np.full((2, 32), -0.0)
+    x[1, :2] = [1.0, 1.0]                        # output i is 1 + (-1)^i: 2 at even i, an exact 0 at odd i
+    v = oracle.hadamard32_rounded(x)
+    assert not np.signbit(v[0]).any() and (v[0] == 0).all()
+    assert (v[1, ::2] == 2.0).all() and not np.signbit(v[1, 1::2]).any() and (v[1, 1::2] == 0).all()
+    qx, sx, _, _ = oracle.rotate_residual_quantize(x)
+    assert (qx[0] == 0).all()                    # +0 encodes as code 0, not 8
