@@ -31,16 +31,17 @@
 //    activation and folded into the weight): each 32-block is multiplied by
 //    the unnormalised 32 x 32 Sylvester Hadamard matrix H, and each output,
 //    the exact sum of the block's 32 values with signs (over 32 for the
-//    weight), is rounded once to fp32. The sums are formed in fp64 by five
-//    butterfly passes of spans 1, 2, 4 (inside a lane) and 8, 16 (across the
-//    block's four lanes, DPP), each taking (a, b) at (i, i + span) to
-//    (a + b, a - b); they are exact whenever the block's terms span at most
-//    53 bits (a bf16 block whose nonzero values span at most 40 binades, an
-//    fp32 one 24), and then the one fp64 -> fp32 conversion is the only
-//    rounding. Activations quantize X H; weights W H / 32 (an exact power of
-//    two), so the GEMM returns X W^T unchanged. Codes are decided on the
-//    rotated fp32 values; the residual stays exact (|R| is at most half an
-//    E2M1 step, so R = v - deq(v) loses no bits in fp32);
+//    weight), is rounded once to fp32. Here one lane owns a whole block
+//    (its 64 or 128 bytes as 16-byte loads), so the transform needs no
+//    cross-lane moves: five in-lane fp64 butterfly passes of spans 1, 2, 4,
+//    8, 16, each taking (a, b) at (i, i + span) to (a + b, a - b). The sums
+//    are exact whenever the block's terms span at most 53 bits (a bf16
+//    block whose nonzero values span at most 40 binades, an fp32 one 24),
+//    and then the one fp64 -> fp32 conversion is the only rounding.
+//    Activations quantize X H; weights W H / 32 (an exact power of two), so
+//    the GEMM returns X W^T unchanged. Codes are decided on the rotated fp32
+//    values; the residual stays exact (|R| is at most half an E2M1 step, so
+//    R = v - deq(v) loses no bits in fp32);
 //  * MXFP8 output ("Activation Outliers Matter", Abstract and §1 study MXFP8
 //    beside MXFP4; elements per OCP MX v1.0): E4M3 codes, one byte per
 //    element, with se = max(floor(log2 amax) - 8, -127), either for X itself
@@ -107,47 +108,24 @@ __device__ __forceinline__ void store_part(uint8_t* q, uint32_t g, uint32_t part
     __builtin_nontemporal_store(c.x, reinterpret_cast<unsigned*>(q + (uint64_t)g * 16 + part * 4));
 }
 
-// One fp64 butterfly pass across lanes: this lane's element pairs with the
-// same element of lane (lane ^ kXor) in its quad; the lane with the span bit
-// clear keeps a + b, the other a - b (a = the clear lane's value). The
-// partner's value comes over as two 32-bit DPP moves. (a - b is formed as
-// (-b) + a: negation is exact, so it is the same IEEE sum.)
-template <int kDpp>
-__device__ __forceinline__ void butterfly_across_f64(double* v, bool upper) {
-  const uint64_t flip = upper ? 0x8000000000000000ull : 0ull;
+// Walsh-Hadamard transform of one 32-block held whole by this lane,
+// unnormalised (times 1/32 with div32, an exact scaling in fp64): the sums
+// in fp64 by five butterfly passes, then one rounding of each to fp32. A
+// sum that is exactly zero comes out as +0, whatever the signs of the zeros
+// summed (IEEE gives -0 + -0 = -0, so the passes alone would keep -0 for
+// some sums of negative zeros).
+__device__ __forceinline__ void hadamard32_lane(double* v, float* f, bool div32) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v[j]);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, kDpp, 0xF, 0xF, true);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), kDpp, 0xF, 0xF, true);
-    const double o = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-    v[j] = __builtin_bit_cast(double, u ^ flip) + o;
-  }
-}
-
-// Walsh-Hadamard transform of the 32-block held by a quad of lanes (lane part
-// p holds elements 8 p .. 8 p + 7), unnormalised (times 1/32 with div32, an
-// exact scaling in fp64): the sums in fp64 by the passes above, then one
-// rounding of each to fp32. A sum that is exactly zero comes out as +0,
-// whatever the signs of the zeros summed (IEEE gives -0 + -0 = -0, so the
-// passes alone would keep -0 for a block of negative zeros).
-__device__ __forceinline__ void hadamard32(float* f, unsigned part, bool div32) {
-  double v[8];
+  for (int span = 1; span < 32; span *= 2)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (double)f[j];
-#pragma unroll
-  for (int span = 1; span < 8; span *= 2)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 32; ++j)
       if (!(j & span)) {
         const double a = v[j], b = v[j + span];
         v[j] = a + b;
         v[j + span] = a - b;
       }
-  butterfly_across_f64<kQuadXor1>(v, part & 1);   // span 8
-  butterfly_across_f64<kQuadXor2>(v, part & 2);   // span 16
 #pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = (float)((div32 ? v[j] * 0.03125 : v[j]) + 0.0);   // + 0: an exact zero is +0
+  for (int j = 0; j < 32; ++j) f[j] = (float)((div32 ? v[j] * 0.03125 : v[j]) + 0.0);   // + 0: an exact zero is +0
 }
 
 // max over 8 fp32 magnitudes as a bit pattern (monotone in the value for
@@ -172,15 +150,18 @@ struct QuantParams {
 
 // kXFmt: format of Q(X), 4 (E2M1) or 8 (E4M3). kRFmt: format of Q(R), 0 for
 // no residual pass (the residual needs an E2M1 Q(X)). kF32In: X is fp32
-// (else bf16). kRotate: 0 none, 1 X H (activations), 2 X H / 32 (weights).
-template <int kXFmt, int kRFmt, bool kF32In, int kRotate>
+// (else bf16).
+template <int kXFmt, int kRFmt, bool kF32In>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   constexpr bool kResidual = kRFmt != 0;
-  static_assert(kXFmt == 4 || (kXFmt == 8 && !kResidual && kRotate == 0), "format combination");
+  static_assert(kXFmt == 4 || (kXFmt == 8 && !kResidual), "format combination");
   const unsigned lane = threadIdx.x & 63;
   const unsigned wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const uint32_t g0 = wave * kBlocksPerWave;   // first block of this wave
-  if (g0 >= p.total_blocks) return;
+  // first block of this wave, and how many blocks are left from it (64-bit
+  // first: the block count may come close to 2^32)
+  if ((uint64_t)wave * kBlocksPerWave >= p.total_blocks) return;
+  const uint32_t g0 = wave * kBlocksPerWave;
+  const uint32_t left = p.total_blocks - g0;
   const uint32_t quad = lane >> 2, part = lane & 3;
 
   // row/column of each unit's block for this lane
@@ -193,38 +174,34 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   uint32_t gblk[kUnits];
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
-    uint32_t g = g0 + u * 16 + quad;
+    const uint32_t g = g0 + u * 16 + quad;
     uint32_t b = col0 + u * 16 + quad, r = row0;
     while (b >= p.nblk_row) { b -= p.nblk_row; ++r; }
     gblk[u] = g;
+    const bool valid = u * 16 + quad < left;
     const int64_t elem = (int64_t)r * p.ldx + (int64_t)b * 32 + part * 8;
     const u32x4_t* src = kF32In ? reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + elem)
                                 : reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + elem);
 #pragma unroll
-    for (int h = 0; h < kLoads; ++h) w[u][h] = (g < p.total_blocks) ? __builtin_nontemporal_load(src + h) : u32x4_t{0, 0, 0, 0};
+    for (int h = 0; h < kLoads; ++h) w[u][h] = valid ? __builtin_nontemporal_load(src + h) : u32x4_t{0, 0, 0, 0};
   }
 
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
     const uint32_t g = gblk[u];
-    const bool valid = g < p.total_blocks;
+    const bool valid = u * 16 + quad < left;
     float xf[8];
     unsigned e;                                        // biased exponent of the block amax (fp32/bf16 field)
-    if (!kF32In && kRotate == 0) {
+    if (!kF32In) {
       const unsigned amax = quad_max_u32(bf16x8_absmax_bits(w[u][0]));
       e = amax >> 7;
       widen_bf16x8(w[u][0], xf);
     } else {
-      if (kF32In) {
-        // (whole-vector bit casts: a bit cast of a single ext-vector element
-        // has been seen to read element 0)
-        const f32x4_t lo = __builtin_bit_cast(f32x4_t, w[u][0]), hi = __builtin_bit_cast(f32x4_t, w[u][kLoads - 1]);
-        xf[0] = lo.x; xf[1] = lo.y; xf[2] = lo.z; xf[3] = lo.w;
-        xf[4] = hi.x; xf[5] = hi.y; xf[6] = hi.z; xf[7] = hi.w;
-      } else {
-        widen_bf16x8(w[u][0], xf);
-      }
-      if (kRotate != 0) hadamard32(xf, part, kRotate == 2);
+      // (whole-vector bit casts: a bit cast of a single ext-vector element
+      // has been seen to read element 0)
+      const f32x4_t lo = __builtin_bit_cast(f32x4_t, w[u][0]), hi = __builtin_bit_cast(f32x4_t, w[u][kLoads - 1]);
+      xf[0] = lo.x; xf[1] = lo.y; xf[2] = lo.z; xf[3] = lo.w;
+      xf[4] = hi.x; xf[5] = hi.y; xf[6] = hi.z; xf[7] = hi.w;
       e = quad_max_u32(f32x8_absmax_bits(xf)) >> 23;
     }
     const bool nonfinite = e == 255;
@@ -263,16 +240,159 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   }
 }
 
+// max |f[j]| over 32 fp32 values as a float (a NaN operand of max is dropped
+// unless both are NaN).
+__device__ __forceinline__ float absmax32(const float* f) {
+  float m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = fmaxf(fmaxf(fabsf(f[4 * j]), fabsf(f[4 * j + 1])), fmaxf(fabsf(f[4 * j + 2]), fabsf(f[4 * j + 3])));
+#pragma unroll
+  for (int k = 4; k >= 1; k /= 2)
+#pragma unroll
+    for (int j = 0; j < k; ++j) m[j] = fmaxf(m[j], m[j + k]);
+  return m[0];
+}
+
+// The rotated passes, one 32-block per lane: X H with the E2M1 residual
+// pass (kRotate 1, activations) or W H / 32 to plain E2M1 (kRotate 2,
+// weights). A wave covers 64 consecutive blocks; each lane transforms and
+// encodes one block and writes its 16 code bytes and its scale byte, so the
+// code and scale stores of a wave are contiguous.
+template <bool kF32In, int kRotate>
+__global__ __launch_bounds__(kThreads) void rotate_quantize_kernel(QuantParams p) {
+  constexpr bool kResidual = kRotate == 1;
+  const unsigned lane = threadIdx.x & 63;
+  const unsigned wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  // (64-bit first: the block count may come close to 2^32; waves past the
+  // end stay to the barrier below and skip their loads and stores)
+  const bool wave_live = (uint64_t)wave * 64 < p.total_blocks;
+  const uint32_t g0 = wave * 64;
+  const uint32_t left = wave_live ? p.total_blocks - g0 : 0u;
+  const uint32_t g = g0 + lane;
+  const bool valid = lane < left;
+  const uint32_t row0 = wave_live ? g0 / p.nblk_row : 0u, col0 = g0 - row0 * p.nblk_row;
+
+  // A block's bytes as 16-byte chunks. bf16: each lane loads its own 64
+  // bytes (4 loads; each instruction takes 16 bytes of every 64 across the
+  // wave's 4 KB), with ordinary loads: non-temporal ones measured 42%
+  // slower in this pattern (329 against 232 us on a 32768 x 13824 layer).
+  // fp32: direct loads of a lane's 128 bytes measured 519 us there, so the
+  // wave loads its 8 KB contiguously (1 KB per instruction, lane l taking
+  // chunk l) and transposes it through LDS (374 us), with one padding
+  // chunk per block so that the per-lane reads are free of bank conflicts.
+  constexpr int kLoads = kF32In ? 8 : 4;
+  u32x4_t w[kLoads];
+  if constexpr (!kF32In) {
+    uint32_t b = col0 + lane, r = row0;
+    while (b >= p.nblk_row) { b -= p.nblk_row; ++r; }
+    const u32x4_t* src =
+        reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + (valid ? (int64_t)r * p.ldx + (int64_t)b * 32 : 0));
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) w[h] = valid ? src[h] : u32x4_t{0, 0, 0, 0};
+  } else {
+    constexpr int kStride = kLoads * 16 + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads / 64][64 * kStride];
+    uint8_t* ws = stage[threadIdx.x >> 6];
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) {
+      const uint32_t c = h * 64 + lane, blk = c / kLoads, chunk = c % kLoads;
+      uint32_t b = col0 + blk, r = row0;
+      while (b >= p.nblk_row) { b -= p.nblk_row; ++r; }
+      const bool ok = blk < left;
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+          static_cast<const float*>(p.x) + (ok ? (int64_t)r * p.ldx + (int64_t)b * 32 + chunk * 4 : 0));
+      w[h] = ok ? __builtin_nontemporal_load(src) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) {
+      const uint32_t c = h * 64 + lane;
+      *reinterpret_cast<u32x4_t*>(ws + (c / kLoads) * kStride + (c % kLoads) * 16) = w[h];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) w[h] = *reinterpret_cast<const u32x4_t*>(ws + lane * kStride + h * 16);
+  }
+
+  double v[32];
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) {
+    if constexpr (kF32In) {
+      const f32x4_t q = __builtin_bit_cast(f32x4_t, w[h]);
+      v[4 * h] = q.x; v[4 * h + 1] = q.y; v[4 * h + 2] = q.z; v[4 * h + 3] = q.w;
+    } else {
+      float f[8];
+      widen_bf16x8(w[h], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[8 * h + j] = f[j];
+    }
+  }
+  float xf[32];
+  hadamard32_lane(v, xf, kRotate == 2);
+
+  // Block amax by float max over magnitudes. Max drops a NaN operand, but
+  // here non-finite values never mix with finite ones in a block: a NaN or
+  // an infinity among the inputs reaches every one of the 32 sums, as a
+  // NaN or an infinity, and an fp32 overflow of a sum gives an infinity
+  // that the max keeps; a block of NaNs gives a NaN. Either way the
+  // exponent field reads 255.
+  const unsigned e = __builtin_bit_cast(unsigned, absmax32(xf)) >> 23;
+  const bool nonfinite = e == 255;
+  const unsigned sxc = nonfinite ? 255u : (e > 2u ? e - 2u : 0u);
+  const float s = scale_operand(sxc);
+  u32x4_t cx;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cx[q] = nonfinite ? 0u : encode_f32x8(xf + 8 * q, s);
+
+  u32x4_t cr = {0u, 0u, 0u, 0u};
+  unsigned src_code = 255u;
+  if constexpr (kResidual) {
+    float rr[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned c = cx[q];
+      residual_pair<0>(xf + 8 * q, c, s, rr + 8 * q);
+      residual_pair<1>(xf + 8 * q, c, s, rr + 8 * q);
+      residual_pair<2>(xf + 8 * q, c, s, rr + 8 * q);
+      residual_pair<3>(xf + 8 * q, c, s, rr + 8 * q);
+    }
+    const unsigned er = __builtin_bit_cast(unsigned, absmax32(rr)) >> 23;   // (R is finite when X is)
+    const unsigned rc = er > 2u ? er - 2u : 0u;
+    const float sr = scale_operand(rc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cr[q] = nonfinite ? 0u : encode_f32x8(rr + 8 * q, sr);
+    src_code = nonfinite ? 255u : rc;
+  }
+
+  if (valid) {
+    __builtin_nontemporal_store(cx, reinterpret_cast<u32x4_t*>(p.qx + (uint64_t)g * 16));
+    p.sx[g] = (uint8_t)sxc;
+    if constexpr (kResidual) {
+      __builtin_nontemporal_store(cr, reinterpret_cast<u32x4_t*>(p.qr + (uint64_t)g * 16));
+      p.sr[g] = (uint8_t)src_code;
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
 
-template <int kXFmt, int kRFmt, int kRotate>
+template <int kXFmt, int kRFmt>
 void launch_one(bool x_f32, dim3 grid, dim3 block, hipStream_t stream, const QuantParams& p) {
   if (x_f32)
-    hipLaunchKernelGGL((quantize_kernel<kXFmt, kRFmt, true, kRotate>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((quantize_kernel<kXFmt, kRFmt, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((quantize_kernel<kXFmt, kRFmt, false, kRotate>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((quantize_kernel<kXFmt, kRFmt, false>), grid, block, 0, stream, p);
+}
+
+template <int kRotate>
+void launch_rotated(bool x_f32, hipStream_t stream, const QuantParams& p) {
+  const uint64_t waves = ((uint64_t)p.total_blocks + 63) / 64;
+  const dim3 grid((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64))), block(kThreads);
+  if (x_f32)
+    hipLaunchKernelGGL((rotate_quantize_kernel<true, kRotate>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((rotate_quantize_kernel<false, kRotate>), grid, block, 0, stream, p);
 }
 
 }  // namespace
@@ -288,7 +408,7 @@ hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int x_fmt, int
   p.sr = sr;
   p.nblk_row = (uint32_t)(K / 32);
   p.total_blocks = (uint32_t)(rows * (K / 32));
-  const uint64_t waves = (p.total_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
+  const uint64_t waves = ((uint64_t)p.total_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
   const uint64_t groups = (waves + kThreads / 64 - 1) / (kThreads / 64);
   const dim3 grid((unsigned)groups), block(kThreads);
   if (qr == nullptr) r_fmt = 0;
@@ -296,12 +416,12 @@ hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int x_fmt, int
   // with plain E2M1 (weights); E4M3 output only without rotation
   const int key = rotate * 100 + x_fmt * 10 + r_fmt;
   switch (key) {
-    case 40: launch_one<4, 0, 0>(x_f32, grid, block, stream, p); break;
-    case 44: launch_one<4, 4, 0>(x_f32, grid, block, stream, p); break;
-    case 48: launch_one<4, 8, 0>(x_f32, grid, block, stream, p); break;
-    case 80: launch_one<8, 0, 0>(x_f32, grid, block, stream, p); break;
-    case 144: launch_one<4, 4, 1>(x_f32, grid, block, stream, p); break;
-    case 240: launch_one<4, 0, 2>(x_f32, grid, block, stream, p); break;
+    case 40: launch_one<4, 0>(x_f32, grid, block, stream, p); break;
+    case 44: launch_one<4, 4>(x_f32, grid, block, stream, p); break;
+    case 48: launch_one<4, 8>(x_f32, grid, block, stream, p); break;
+    case 80: launch_one<8, 0>(x_f32, grid, block, stream, p); break;
+    case 144: launch_rotated<1>(x_f32, stream, p); break;
+    case 240: launch_rotated<2>(x_f32, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -159,6 +159,32 @@ def test_rotation_is_the_exact_sum_rounded_once(dtype):
     check_mx(got_w, oracle.rotate_quantize_weight(w64), f"rotated W {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("rows,K,pad", [(1, 32, 0), (3, 32, 8), (67, 32, 24), (5, 96, 40), (129, 224, 8)])
+def test_rotated_strided_and_ragged(dtype, rows, K, pad):
+    """One block per lane, 64 per wave: fewer blocks than a wave, a ragged
+    last wave, K = 32 (a wave's blocks spread over 64 rows), and rows
+    padded past K (ldx = K + pad, pad a multiple of 8 elements)."""
+    rng = np.random.default_rng(1000 + rows + K + pad)
+    ldx = K + pad
+    full = heavy_f32(rng, rows, ldx) if rows > 1 else rng.normal(0, 3, (1, ldx)).astype(np.float32)
+    log(f"[rotate] strided {dtype} rows={rows} K={K} ldx={ldx}")
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(full)
+        xd = dev_bf16(bits)
+        x64 = oracle.bf16_bits_to_f64(bits[:, :K])
+    else:
+        xd = dev_f32(full)
+        x64 = full[:, :K].astype(np.float64)
+    view = xd[:, :K]
+    assert view.stride(0) == ldx
+    got_x = rfq.rotate_residual_quantize(view)
+    got_w = rfq.rotate_quantize_weight(view)
+    torch.cuda.synchronize()
+    check_rfq(got_x, oracle.rotate_residual_quantize(x64), f"strided rotated X {dtype}")
+    check_mx(got_w, oracle.rotate_quantize_weight(x64), f"strided rotated W {dtype}")
+
+
 @pytest.mark.parametrize("M,N,K", [(130, 200, 512), (64, 96, 160)])
 def test_rotated_layer_every_output(M, N, K):
     """Q(XH), Q(R) and Q(WH/32) from the GPU into the unchanged W4A4 GEMM;
