@@ -270,7 +270,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_kernel(QuantParams p
   const uint32_t left = wave_live ? p.total_blocks - g0 : 0u;
   const uint32_t g = g0 + lane;
   const bool valid = lane < left;
-  const uint32_t row0 = wave_live ? g0 / p.nblk_row : 0u, col0 = g0 - row0 * p.nblk_row;
+  // (row and column of g0 for every wave, so that the row walks below take
+  // at most 1 + 63 / nblk_row steps, in waves past the end too)
+  const uint32_t row0 = g0 / p.nblk_row, col0 = g0 - row0 * p.nblk_row;
 
   // A block's bytes as 16-byte chunks. bf16: each lane loads its own 64
   // bytes (4 loads; each instruction takes 16 bytes of every 64 across the
