@@ -57,7 +57,8 @@ from .quantize import (
     unpack_codes,
 )
 from .gemm import gemm_w4a4, linear
-from .rotate import fraction_to_f32, hadamard32_rounded, linear_rotated, rotate_quantize_weight, rotate_residual_quantize
+from .rotate import (ROTATION_SIZES, fraction_to_f32, hadamard32_rounded, hadamard_rounded, linear_rotated,
+                     rotate_quantize_weight, rotate_residual_quantize)
 from .backward import backward_dw, backward_dx, linear_backward
 from .mxfp8 import (
     E4M3_MAGNITUDES,
@@ -81,7 +82,7 @@ __all__ = [
     "scale_exponent", "encode_block_elements", "quantize_mxfp4", "residual_quantize",
     "dequantize", "pack_codes", "unpack_codes",
     "gemm_w4a4", "linear",
-    "hadamard32_rounded", "fraction_to_f32", "rotate_residual_quantize", "rotate_quantize_weight", "linear_rotated",
+    "hadamard32_rounded", "hadamard_rounded", "ROTATION_SIZES", "fraction_to_f32", "rotate_residual_quantize", "rotate_quantize_weight", "linear_rotated",
     "E4M3_MAGNITUDES", "E4M3_MAX", "e4m3_value", "scale_exponent_e4m3", "encode_e4m3",
     "quantize_mxfp8", "dequantize_mxfp8", "residual_quantize_fp8",
     "gemm_w4a8", "gemm_w4a4_fp8_residual", "linear_w4a8", "linear_fp8_residual",

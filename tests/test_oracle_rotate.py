@@ -169,3 +169,80 @@ def test_an_exact_zero_sum_is_positive_zero():
     assert (v[1, ::2] == 2.0).all() and not np.signbit(v[1, 1::2]).any() and (v[1, 1::2] == 0).all()
     qx, sx, _, _ = oracle.rotate_residual_quantize(x)
     assert (qx[0] == 0).all()                    # +0 encodes as code 0, not 8
+
+
+# ---- the 64-point rotation (the page's per-head size; two MX blocks) ----
+
+H64 = scipy.linalg.hadamard(64).astype(np.float64)
+
+
+def test_size64_is_the_sylvester_matrix_on_exact_inputs():
+    rng = np.random.default_rng(10)
+    x = rng.integers(-8, 9, size=(5, 192)).astype(np.float64)
+    got = oracle.hadamard_rounded(x, 64).astype(np.float64)
+    assert np.array_equal(got, (x.reshape(5, 3, 64) @ H64).reshape(5, 192))
+
+
+def test_size64_is_two_32_point_transforms_combined():
+    """Sylvester's block form H64 = [[H32, H32], [H32, -H32]]: with y0, y1
+    the 32-point transforms of a block's halves, the 64-point transform is
+    [y0 + y1, y0 - y1] (exact inputs, so every sum is exact)."""
+    rng = np.random.default_rng(11)
+    x = rng.integers(-50, 51, size=(4, 128)).astype(np.float64)
+    y = oracle.hadamard_rounded(x, 32).astype(np.float64).reshape(4, 2, 2, 32)
+    want = np.concatenate([y[:, :, 0] + y[:, :, 1], y[:, :, 0] - y[:, :, 1]], axis=2).reshape(4, 128)
+    assert np.array_equal(oracle.hadamard_rounded(x, 64).astype(np.float64), want)
+
+
+def test_size64_outputs_are_exact_sums_rounded_once():
+    rng = np.random.default_rng(12)
+    x = (rng.uniform(1, 2, (6, 64)) * np.exp2(rng.integers(0, 10, (6, 64)))
+         * rng.choice([-1, 1], (6, 64))).astype(np.float32).astype(np.float64)
+    for div in (False, True):
+        got = oracle.hadamard_rounded(x, 64, divide=div)
+        for r in range(6):
+            for i in range(64):
+                q = sum(Fraction(float(x[r, j])) * int(H64[j, i]) for j in range(64))
+                if div:
+                    q /= 64
+                assert Fraction(float(q)) == q
+                assert got[r, i] == np.float32(float(q)), (r, i)
+
+
+def test_size64_twice_is_64_times_identity():
+    rng = np.random.default_rng(13)
+    x = rng.integers(-20, 21, size=(3, 128)).astype(np.float64)
+    once = oracle.hadamard_rounded(x, 64).astype(np.float64)
+    assert np.array_equal(oracle.hadamard_rounded(once, 64).astype(np.float64), 64 * x)
+
+
+def test_size64_rotation_cancels_in_the_layer_when_quantization_is_exact():
+    rng = np.random.default_rng(14)
+    M, N, K = 5, 4, 128
+    V, U = grid_blocks(rng, M, K), grid_blocks(rng, N, K)
+    X = (V.reshape(M, 2, 64) @ H64 / 64).reshape(M, K)
+    W = (U.reshape(N, 2, 64) @ H64).reshape(N, K)
+    assert np.array_equal(X.astype(np.float32).astype(np.float64), X)
+    assert np.array_equal(W.astype(np.float32).astype(np.float64), W)
+    y, s, (qx, sx, qr, sr), (wq, sw) = oracle.linear_rotated(X, W, size=64)
+    assert np.array_equal(oracle.dequantize(qx, sx), V)
+    assert np.array_equal(oracle.dequantize(wq, sw), U)
+    assert (oracle.dequantize(qr, sr) == 0).all()
+    assert np.array_equal(y, X @ W.T)
+
+
+def test_size64_weight_side_carries_the_one_over_64():
+    rng = np.random.default_rng(15)
+    w = rng.normal(0, 0.02, (3, 128)).astype(np.float32).astype(np.float64)
+    wq, sw = oracle.rotate_quantize_weight(w, 64)
+    q0, s0 = oracle.quantize_mxfp4(oracle.hadamard_rounded(w, 64).astype(np.float64))
+    assert np.array_equal(wq, q0)
+    assert np.array_equal(sw.astype(int), s0.astype(int) - 6)
+
+
+def test_rotation_size_and_width_are_checked():
+    import pytest
+    with pytest.raises(ValueError):
+        oracle.hadamard_rounded(np.zeros((1, 96)), 64)
+    with pytest.raises(ValueError):
+        oracle.hadamard_rounded(np.zeros((1, 96)), 48)
