@@ -14,7 +14,8 @@ Prints one JSON line (rank 0) with the effective TFLOP/s of the step
 (4 M N K per step: the contraction over the doubled K), the per-kernel
 rooflines measured with HIP events on the launch stream, and the CPU oracle
 timed on a bounded sample of the same workload. Beside the layer it times,
-on the same X and weight: the block-Hadamard-rotated quantize pass, the
+on the same X and weight: the block-Hadamard-rotated quantize passes (32- and
+64-point), the
 plain W4A4 GEMM, and the MXFP8 variants (W4A8; RFQ with an MXFP8 residual),
 each with its own quantize pass.
 """
@@ -395,6 +396,11 @@ def main():
                                                         qr.data_ptr(), sr.data_ptr(), sp))
     rot_ms = batch_ms(rotated_quantize, 100)
 
+    def rotated64_quantize():
+        rfq._lib.check(lib.rfq_rotate64_residual_quantize(x.data_ptr(), 0, M, K, x.stride(0), qx.data_ptr(),
+                                                          sx.data_ptr(), qr.data_ptr(), sr.data_ptr(), sp))
+    rot64_ms = batch_ms(rotated64_quantize, 100)
+
     flops = 4.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -526,6 +532,13 @@ def main():
                 "pct_hbm_peak": round(100 * QUANT_BYTES_PER_ELEM * M * K / (rot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                 "what": "32-point block Hadamard of X fused before the RFQ pass (rfq_rotate_residual_quantize)",
             },
+            "quantize_residual_rotated64": {
+                "avg_launch_us": round(rot64_ms * 1e3, 2),
+                "GB_per_s": round(QUANT_BYTES_PER_ELEM * M * K / (rot64_ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * QUANT_BYTES_PER_ELEM * M * K / (rot64_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "what": "64-point block Hadamard (two MX blocks) of X fused before the RFQ pass "
+                        "(rfq_rotate64_residual_quantize)",
+            },
             "gemm_rfq": {
                 "avg_launch_us": round(gemm_ms * 1e3, 2),
                 "TFLOP_per_s": round(gemm_tflops, 1),
@@ -624,6 +637,12 @@ def main():
                                                             s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
         q5r_ms = batch_ms(q5_rot, 40, warm=20)
         gbs_rot = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5r_ms * 1e-3) / 1e9
+
+        def q5_rot64():
+            rfq._lib.check(lib.rfq_rotate64_residual_quantize(x5.data_ptr(), 0, c5.M, c5.K, c5.K, q5[0].data_ptr(),
+                                                              s5[0].data_ptr(), q5[1].data_ptr(), s5[1].data_ptr(), sp))
+        q5r64_ms = batch_ms(q5_rot64, 40, warm=20)
+        gbs_rot64 = QUANT_BYTES_PER_ELEM * c5.M * c5.K / (q5r64_ms * 1e-3) / 1e9
         if not args.no_sweep and "dit_ffn_down" not in sweep:
             w5q, w5s = rfq.quantize_mxfp4(to_dev(workloads.w_bf16(c5)))
             sweep["dit_ffn_down"] = layer_timings(rfq, torch, c5, x5, w5q, w5s, batch_ms, 10)
@@ -657,6 +676,12 @@ def main():
             "avg_launch_us": round(q5r_ms * 1e3, 2),
             "GB_per_s": round(gbs_rot, 1),
             "pct_hbm_peak": round(100 * gbs_rot / HBM_PEAK_GBS, 2),
+        }
+        out["kernels"]["quantize_residual_rotated64_dit_ffn_down"] = {
+            "shape": [c5.M, c5.K],
+            "avg_launch_us": round(q5r64_ms * 1e3, 2),
+            "GB_per_s": round(gbs_rot64, 1),
+            "pct_hbm_peak": round(100 * gbs_rot64 / HBM_PEAK_GBS, 2),
         }
         out["kernels"]["hbm_device_copy_reference"] = {
             "bytes_moved": 2 * (1 << 30), "GB_per_s": round(copy_gbs, 1),

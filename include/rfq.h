@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RFQ_ABI_VERSION 7
+#define RFQ_ABI_VERSION 8
 
 typedef enum rfq_status {
   RFQ_OK = 0,
@@ -139,6 +139,25 @@ rfq_status_t rfq_rotate_residual_quantize(const void* x, int x_dtype, int64_t M,
                                           uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream);
 rfq_status_t rfq_rotate_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
                                         uint8_t* codes, uint8_t* scales, rfq_stream_t stream);
+
+/*
+ * The same two passes with a 64-point Hadamard H64 (the page's per-head
+ * rotation size; Sylvester order, H64[i][j] = (-1)^popcount(i & j)) applied
+ * to every 64 elements along K, i.e. to each pair of adjacent MX blocks:
+ * X H64 with the residual pass, and W H64 / 64 for the weight (H64 H64^T =
+ * 64 I, so rfq_gemm_w4a4 again returns X W^T up to quantization). Each
+ * value is the exact 64-term sum (over 64 for the weight) rounded once to
+ * fp32, a zero sum being +0; the sums are exact when a block's terms lie
+ * within 53 bits of each other (nonzero bf16 values within 39 binades, fp32
+ * within 23). K must be a multiple of 64 (RFQ_ERR_INVALID_SHAPE otherwise);
+ * arguments, layouts and other errors as the 32-point calls. Quantization
+ * blocks stay 32 elements.
+ */
+rfq_status_t rfq_rotate64_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                            uint8_t* qx_codes, uint8_t* qx_scales,
+                                            uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream);
+rfq_status_t rfq_rotate64_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                          uint8_t* codes, uint8_t* scales, rfq_stream_t stream);
 
 /*
  * rfq_gemm_w4a4 - block-scaled FP4 GEMM, K-doubled for RFQ:

@@ -150,18 +150,21 @@ def _y_code(y):
     return DTYPE_FP32 if y.dtype == torch.float32 else DTYPE_BF16
 
 
-def _quantize(fn, x, bytes_per_element=0.5):
+def _quantize(name, x, bytes_per_element=0.5):
+    """Entry point `name` on X after X's checks (the library is loaded only then)."""
     rows, K = check_x(x)
     check_device(x.device, x=x)
+    fn = getattr(load(), name)
     codes = torch.empty((rows, int(K * bytes_per_element)), dtype=torch.uint8, device=x.device)
     scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
     check(fn(_ptr(x), _x_code(x), rows, K, x.stride(0), _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
 
 
-def _residual(fn, x, r_bytes_per_element=0.5):
+def _residual(name, x, r_bytes_per_element=0.5):
     M, K = check_x(x)
     check_device(x.device, x=x)
+    fn = getattr(load(), name)
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     qr = torch.empty((M, int(K * r_bytes_per_element)), dtype=torch.uint8, device=x.device)
     sx = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
@@ -172,22 +175,34 @@ def _residual(fn, x, r_bytes_per_element=0.5):
 
 def quantize_mxfp4(x):
     """MXFP4 along K of bf16 or fp32 X: returns (codes uint8 [rows, K/2], scales uint8 [rows, K/32])."""
-    return _quantize(load().rfq_quantize_mxfp4, x)
+    return _quantize("rfq_quantize_mxfp4", x)
 
 
 def residual_quantize(x):
     """RFQ encoding of X: returns (qx, sx, qr, sr) = Q(X) codes/scales, Q(R) codes/scales."""
-    return _residual(load().rfq_residual_quantize, x)
+    return _residual("rfq_residual_quantize", x)
 
 
-def rotate_residual_quantize(x):
-    """RFQ encoding of X H (32-point block Hadamard along K): (qx, sx, qr, sr)."""
-    return _residual(load().rfq_rotate_residual_quantize, x)
+ROTATION_SIZES = (32, 64)
 
 
-def rotate_quantize_weight(w):
-    """MXFP4 codes and scales of W H / 32, the weight side of the rotated layer."""
-    return _quantize(load().rfq_rotate_quantize_weight, w)
+def _rotation_size(x, size):
+    if size not in ROTATION_SIZES:
+        raise ValueError(f"rotation size must be 32 or 64, got {size}")
+    if x.dim() == 2 and x.shape[1] % size:
+        raise ValueError(f"K = {x.shape[1]} must be a multiple of the rotation size {size}")
+
+
+def rotate_residual_quantize(x, size=32):
+    """RFQ encoding of X H (block Hadamard of `size` 32 or 64 along K): (qx, sx, qr, sr)."""
+    _rotation_size(x, size)
+    return _residual("rfq_rotate_residual_quantize" if size == 32 else "rfq_rotate64_residual_quantize", x)
+
+
+def rotate_quantize_weight(w, size=32):
+    """MXFP4 codes and scales of W H / size, the weight side of the rotated layer."""
+    _rotation_size(w, size)
+    return _quantize("rfq_rotate_quantize_weight" if size == 32 else "rfq_rotate64_quantize_weight", w)
 
 
 def gemm_shapes(qx, sx, qr, sr, wq, sw, x_bytes=0.5, r_bytes=0.5):
@@ -220,12 +235,12 @@ def gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.bfloat16, out=None):
 
 def quantize_mxfp8(x):
     """MXFP8 (E4M3) along K of bf16 or fp32 X: (codes uint8 [rows, K], scales uint8 [rows, K/32])."""
-    return _quantize(load().rfq_quantize_mxfp8, x, bytes_per_element=1)
+    return _quantize("rfq_quantize_mxfp8", x, bytes_per_element=1)
 
 
 def residual_quantize_mxfp8(x):
     """RFQ encoding with an MXFP8 second path: (qx [M, K/2], sx, qr8 [M, K], sr)."""
-    return _residual(load().rfq_residual_quantize_mxfp8, x, r_bytes_per_element=1)
+    return _residual("rfq_residual_quantize_mxfp8", x, r_bytes_per_element=1)
 
 
 def gemm_w4a8(qx8, sx, wq, sw, out_dtype=torch.bfloat16, out=None):

@@ -28,6 +28,8 @@ SIGNATURES = {
     "rfq_residual_quantize": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "rfq_rotate_residual_quantize": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "rfq_rotate_quantize_weight": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p]),
+    "rfq_rotate64_residual_quantize": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "rfq_rotate64_quantize_weight": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p]),
     "rfq_gemm_w4a4": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i, _i64, _p]),
     "rfq_linear_workspace_size": (_sz, [_i64, _i64]),
     "rfq_linear": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _i64, _p, _i, _i64, _p, _sz, _p]),

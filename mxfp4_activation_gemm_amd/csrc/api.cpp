@@ -46,6 +46,13 @@ rfq_status_t check_rows_k(int64_t rows, int64_t K, const char* rname) {
   return RFQ_OK;
 }
 
+// The 64-point rotation spans two MX blocks: K a multiple of 64.
+rfq_status_t check_k64(int64_t K) {
+  if (K % 64 != 0)
+    return fail(RFQ_ERR_INVALID_SHAPE, "K = %lld must be a multiple of 64 for the 64-point rotation", (long long)K);
+  return RFQ_OK;
+}
+
 // A GEMM output Y [M, N] holds fewer than 2^40 elements (the tile count
 // stays in 32-bit arithmetic).
 rfq_status_t check_mn(int64_t M, int64_t N) {
@@ -217,6 +224,21 @@ rfq_status_t rfq_rotate_residual_quantize(const void* x, int x_dtype, int64_t M,
 rfq_status_t rfq_rotate_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
                                         uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
   return quantize_common(w, w_dtype, N, K, ldw, codes, scales, 2, 4, stream);
+}
+
+rfq_status_t rfq_rotate64_residual_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                            uint8_t* qx_codes, uint8_t* qx_scales,
+                                            uint8_t* qr_codes, uint8_t* qr_scales, rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(M, K, "M"));
+  RFQ_TRY(check_k64(K));
+  return residual_common(x, x_dtype, M, K, ldx, qx_codes, qx_scales, qr_codes, qr_scales, 3, 4, stream);
+}
+
+rfq_status_t rfq_rotate64_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                          uint8_t* codes, uint8_t* scales, rfq_stream_t stream) {
+  RFQ_TRY(check_rows_k(N, K, "N"));
+  RFQ_TRY(check_k64(K));
+  return quantize_common(w, w_dtype, N, K, ldw, codes, scales, 4, 4, stream);
 }
 
 rfq_status_t rfq_gemm_w4a4(const uint8_t* qx_codes, const uint8_t* qx_scales,

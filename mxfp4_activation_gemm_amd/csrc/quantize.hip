@@ -108,13 +108,9 @@ __device__ __forceinline__ void store_part(uint8_t* q, uint32_t g, uint32_t part
     __builtin_nontemporal_store(c.x, reinterpret_cast<unsigned*>(q + (uint64_t)g * 16 + part * 4));
 }
 
-// Walsh-Hadamard transform of one 32-block held whole by this lane,
-// unnormalised (times 1/32 with div32, an exact scaling in fp64): the sums
-// in fp64 by five butterfly passes, then one rounding of each to fp32. A
-// sum that is exactly zero comes out as +0, whatever the signs of the zeros
-// summed (IEEE gives -0 + -0 = -0, so the passes alone would keep -0 for
-// some sums of negative zeros).
-__device__ __forceinline__ void hadamard32_lane(double* v, float* f, bool div32) {
+// Walsh-Hadamard sums of one 32-block held whole by this lane,
+// unnormalised, in fp64: five butterfly passes.
+__device__ __forceinline__ void hadamard32_sums(double* v) {
 #pragma unroll
   for (int span = 1; span < 32; span *= 2)
 #pragma unroll
@@ -124,8 +120,33 @@ __device__ __forceinline__ void hadamard32_lane(double* v, float* f, bool div32)
         v[j] = a + b;
         v[j + span] = a - b;
       }
+}
+
+// The span-32 pass of a 64-point transform over lanes 2m and 2m + 1, which
+// hold the 32-point sums of the two halves of one 64-block (Sylvester's
+// H64 = [[H32, H32], [H32, -H32]]): the even lane keeps a + b, the odd one
+// a - b, a the even lane's value and b the odd one's. The partner's fp64
+// value comes over as two 32-bit DPP moves; fma(-1, b, a) is a - b with one
+// rounding, as the sum of a and -b.
+__device__ __forceinline__ void hadamard64_pair_pass(double* v, unsigned lane) {
+  const double sign = (lane & 1) ? -1.0 : 1.0;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) f[j] = (float)((div32 ? v[j] * 0.03125 : v[j]) + 0.0);   // + 0: an exact zero is +0
+  for (int j = 0; j < 32; ++j) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v[j]);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, kQuadXor1, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), kQuadXor1, 0xF, 0xF, true);
+    const double o = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    v[j] = __builtin_fma(sign, v[j], o);
+  }
+}
+
+// One rounding of each fp64 sum to fp32, after an exact power-of-two
+// scaling (1, or 1 / n on the weight side). A sum that is exactly zero comes
+// out as +0, whatever the signs of the zeros summed (IEEE gives -0 + -0 =
+// -0, so the passes alone would keep -0 for some sums of negative zeros).
+__device__ __forceinline__ void round_sums(const double* v, float* f, double scale) {
+#pragma unroll
+  for (int j = 0; j < 32; ++j) f[j] = (float)(v[j] * scale + 0.0);
 }
 
 // max over 8 fp32 magnitudes as a bit pattern (monotone in the value for
@@ -254,11 +275,14 @@ __device__ __forceinline__ float absmax32(const float* f) {
 }
 
 // The rotated passes, one 32-block per lane: X H with the E2M1 residual
-// pass (kRotate 1, activations) or W H / 32 to plain E2M1 (kRotate 2,
-// weights). A wave covers 64 consecutive blocks; each lane transforms and
-// encodes one block and writes its 16 code bytes and its scale byte, so the
-// code and scale stores of a wave are contiguous.
-template <bool kF32In, int kRotate>
+// pass (kRotate 1, activations) or W H / n to plain E2M1 (kRotate 2,
+// weights), H of size kSize = 32 (one MX block) or 64 (two adjacent MX
+// blocks of a row, held by lanes 2m and 2m + 1: K is a multiple of 64, so a
+// row has an even number of blocks and every even block starts a pair). A
+// wave covers 64 consecutive blocks; each lane transforms and encodes one
+// block and writes its 16 code bytes and its scale byte, so the code and
+// scale stores of a wave are contiguous.
+template <bool kF32In, int kRotate, int kSize>
 __global__ __launch_bounds__(kThreads) void rotate_quantize_kernel(QuantParams p) {
   constexpr bool kResidual = kRotate == 1;
   const unsigned lane = threadIdx.x & 63;
@@ -329,7 +353,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_kernel(QuantParams p
     }
   }
   float xf[32];
-  hadamard32_lane(v, xf, kRotate == 2);
+  hadamard32_sums(v);
+  if constexpr (kSize == 64) hadamard64_pair_pass(v, lane);
+  round_sums(v, xf, kRotate == 2 ? 1.0 / kSize : 1.0);
 
   // Block amax by float max over magnitudes. Max drops a NaN operand, but
   // here non-finite values never mix with finite ones in a block: a NaN or
@@ -387,14 +413,14 @@ void launch_one(bool x_f32, dim3 grid, dim3 block, hipStream_t stream, const Qua
     hipLaunchKernelGGL((quantize_kernel<kXFmt, kRFmt, false>), grid, block, 0, stream, p);
 }
 
-template <int kRotate>
+template <int kRotate, int kSize>
 void launch_rotated(bool x_f32, hipStream_t stream, const QuantParams& p) {
   const uint64_t waves = ((uint64_t)p.total_blocks + 63) / 64;
   const dim3 grid((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64))), block(kThreads);
   if (x_f32)
-    hipLaunchKernelGGL((rotate_quantize_kernel<true, kRotate>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((rotate_quantize_kernel<true, kRotate, kSize>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((rotate_quantize_kernel<false, kRotate>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((rotate_quantize_kernel<false, kRotate, kSize>), grid, block, 0, stream, p);
 }
 
 }  // namespace
@@ -414,16 +440,19 @@ hipError_t launch_quantize(const void* x, bool x_f32, int rotate, int x_fmt, int
   const uint64_t groups = (waves + kThreads / 64 - 1) / (kThreads / 64);
   const dim3 grid((unsigned)groups), block(kThreads);
   if (qr == nullptr) r_fmt = 0;
-  // rotation 1 goes with the E2M1 residual pass (activations), rotation 2
-  // with plain E2M1 (weights); E4M3 output only without rotation
+  // rotation 1 (3) goes with the E2M1 residual pass (activations), rotation
+  // 2 (4) with plain E2M1 (weights), 32-point (64-point); E4M3 output only
+  // without rotation
   const int key = rotate * 100 + x_fmt * 10 + r_fmt;
   switch (key) {
     case 40: launch_one<4, 0>(x_f32, grid, block, stream, p); break;
     case 44: launch_one<4, 4>(x_f32, grid, block, stream, p); break;
     case 48: launch_one<4, 8>(x_f32, grid, block, stream, p); break;
     case 80: launch_one<8, 0>(x_f32, grid, block, stream, p); break;
-    case 144: launch_rotated<1>(x_f32, stream, p); break;
-    case 240: launch_rotated<2>(x_f32, stream, p); break;
+    case 144: launch_rotated<1, 32>(x_f32, stream, p); break;
+    case 240: launch_rotated<2, 32>(x_f32, stream, p); break;
+    case 344: launch_rotated<1, 64>(x_f32, stream, p); break;
+    case 440: launch_rotated<2, 64>(x_f32, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

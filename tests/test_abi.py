@@ -36,11 +36,11 @@ def declared_functions():
 
 def test_header_declarations_are_exported_and_bound(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
-    assert lib.rfq_abi_version() == 7
+    assert lib.rfq_abi_version() == 8
 
 
 def status_name(st):
@@ -138,6 +138,21 @@ def test_rotated_quantize_validation(lib):
     assert status_name(w(FAKE + 4, 1, 4, 64, 64, FAKE, FAKE, None)) == "RFQ_ERR_MISALIGNED"
     assert status_name(w(FAKE, 0, 4, 64, 64, None, FAKE, None)) == "RFQ_ERR_NULL_POINTER"
     assert status_name(w(None, 0, 0, 64, 64, None, None, None)) == "RFQ_OK"
+
+
+def test_rotated64_quantize_validation(lib):
+    f, w = lib.rfq_rotate64_residual_quantize, lib.rfq_rotate64_quantize_weight
+    # K a multiple of 32 but not of 64: rejected, also with no rows
+    assert status_name(f(FAKE, 0, 4, 96, 96, FAKE, FAKE, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_SHAPE"
+    assert status_name(f(None, 0, 0, 96, 96, None, None, None, None, None)) == "RFQ_ERR_INVALID_SHAPE"
+    assert status_name(w(FAKE, 0, 4, 160, 160, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_SHAPE"
+    assert status_name(f(FAKE, 0, 4, 48, 48, FAKE, FAKE, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_SHAPE"
+    assert status_name(f(FAKE, 0, 4, 128, 128, FAKE, FAKE, None, FAKE, None)) == "RFQ_ERR_NULL_POINTER"
+    assert status_name(f(FAKE, 3, 4, 128, 128, FAKE, FAKE, FAKE, FAKE, None)) == "RFQ_ERR_UNSUPPORTED_DTYPE"
+    assert status_name(f(None, 0, 0, 128, 128, None, None, None, None, None)) == "RFQ_OK"
+    assert status_name(w(FAKE, 1, 4, 128, 126, FAKE, FAKE, None)) == "RFQ_ERR_INVALID_STRIDE"
+    assert status_name(w(FAKE + 4, 1, 4, 128, 128, FAKE, FAKE, None)) == "RFQ_ERR_MISALIGNED"
+    assert status_name(w(None, 0, 0, 128, 128, None, None, None)) == "RFQ_OK"
 
 
 def test_mxfp8_entry_points_validation(lib):

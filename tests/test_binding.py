@@ -153,3 +153,19 @@ def test_backward_rejects():
     raises(lambda: rfq.backward_dw(dy, g["qx"], g["sx"], g["qr"], g["sr"], out=torch.zeros((N, K + 32))),
            "out: has 96 columns")
     raises(lambda: rfq.backward_dw(dy, g["qx"], g["sx"], g["qr"], g["sr"], workspace=torch.zeros(10)), "workspace")
+
+
+@pytest.mark.parametrize("call", ["quantize_mxfp4", "residual_quantize", "rotate_residual_quantize",
+                                  "rotate_quantize_weight", "quantize_mxfp8", "residual_quantize_mxfp8"])
+def test_quantize_calls_check_x_before_the_library(call):
+    fn = getattr(rfq, call)
+    raises(lambda: fn(torch.zeros((M, K), dtype=torch.float16)), "dtype|bf16|fp32|float")     # unsupported dtype
+    raises(lambda: fn(torch.zeros((M, K), dtype=torch.bfloat16)), "CUDA")                     # host tensor
+
+
+def test_rotation_size_is_checked():
+    x = torch.zeros((M, 96), dtype=torch.bfloat16)
+    raises(lambda: rfq.rotate_residual_quantize(x, size=48), "32 or 64")
+    raises(lambda: rfq.rotate_residual_quantize(x, size=64), "multiple of the rotation size 64")
+    raises(lambda: rfq.rotate_quantize_weight(x, size=64), "multiple of the rotation size 64")
+    raises(lambda: rfq.rotate_quantize_weight(torch.zeros((M, 128), dtype=torch.bfloat16), size=64), "CUDA")
