@@ -28,19 +28,22 @@
 //  * fp32 input (8 values = 32 bytes per lane);
 //  * rotation before quantization ("大模型量化中的双线性尾部问题与QuaRot正交旋转
 //    解决方案" §3, QuaRot: an orthogonal +-1 matrix applied online to the
-//    activation and folded into the weight): each 32-block is multiplied by
-//    the unnormalised 32 x 32 Sylvester Hadamard matrix H, and each output,
-//    the exact sum of the block's 32 values with signs (over 32 for the
-//    weight), is rounded once to fp32. Here one lane owns a whole block
-//    (its 64 or 128 bytes as 16-byte loads), so the transform needs no
-//    cross-lane moves: five in-lane fp64 butterfly passes of spans 1, 2, 4,
-//    8, 16, each taking (a, b) at (i, i + span) to (a + b, a - b). The sums
-//    are exact whenever the block's terms span at most 53 bits (a bf16
-//    block whose nonzero values span at most 40 binades, an fp32 one 24),
-//    and then the one fp64 -> fp32 conversion is the only rounding.
-//    Activations quantize X H; weights W H / 32 (an exact power of two), so
-//    the GEMM returns X W^T unchanged. Codes are decided on the rotated fp32
-//    values; the residual stays exact (|R| is at most half an E2M1 step, so
+//    activation and folded into the weight): each n-block along K (n = 32,
+//    one MX block, or 64, two) is multiplied by the unnormalised n x n
+//    Sylvester Hadamard matrix H, and each output, the exact sum of the
+//    block's n values with signs (over n for the weight), is rounded once
+//    to fp32. Here one lane owns a whole MX block (a wave's blocks are
+//    loaded contiguously and transposed through LDS), so the 32-point
+//    transform needs no cross-lane moves: five in-lane fp64 butterfly
+//    passes of spans 1, 2, 4, 8, 16, each taking (a, b) at (i, i + span) to
+//    (a + b, a - b); the 64-point one adds a sixth pass across the lane
+//    pair that holds its two MX blocks. The sums are exact whenever the
+//    block's terms span at most 53 bits (a bf16 block whose nonzero values
+//    span at most 40 binades for n = 32, 39 for n = 64; fp32: 24, 23), and
+//    then the one fp64 -> fp32 conversion is the only rounding. Activations
+//    quantize X H; weights W H / n (an exact power of two), so the GEMM
+//    returns X W^T unchanged. Codes are decided on the rotated fp32 values;
+//    the residual stays exact (|R| is at most half an E2M1 step, so
 //    R = v - deq(v) loses no bits in fp32);
 //  * MXFP8 output ("Activation Outliers Matter", Abstract and §1 study MXFP8
 //    beside MXFP4; elements per OCP MX v1.0): E4M3 codes, one byte per
@@ -298,46 +301,38 @@ __global__ __launch_bounds__(kThreads) void rotate_quantize_kernel(QuantParams p
   // at most 1 + 63 / nblk_row steps, in waves past the end too)
   const uint32_t row0 = g0 / p.nblk_row, col0 = g0 - row0 * p.nblk_row;
 
-  // A block's bytes as 16-byte chunks. bf16: each lane loads its own 64
-  // bytes (4 loads; each instruction takes 16 bytes of every 64 across the
-  // wave's 4 KB), with ordinary loads: non-temporal ones measured 42%
-  // slower in this pattern (329 against 232 us on a 32768 x 13824 layer).
-  // fp32: direct loads of a lane's 128 bytes measured 519 us there, so the
-  // wave loads its 8 KB contiguously (1 KB per instruction, lane l taking
-  // chunk l) and transposes it through LDS (374 us), with one padding
-  // chunk per block so that the per-lane reads are free of bank conflicts.
+  // A block's bytes as 16-byte chunks (4 for bf16, 8 for fp32). The wave
+  // loads its 64 blocks contiguously (1 KB per instruction, lane l taking
+  // chunk l) and transposes them through LDS to one block per lane, with one
+  // padding chunk per block so that the per-lane reads are free of bank
+  // conflicts. Loading each lane's own block directly (4 or 8 loads that
+  // each take 16 bytes of every 64 or 128 across the wave) measured 232
+  // against 253 us on one box and 280 against 239 us on another for bf16 X
+  // on a 32768 x 13824 layer, and 519 against 374 us for fp32 X.
   constexpr int kLoads = kF32In ? 8 : 4;
+  constexpr int kStride = kLoads * 16 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads / 64][64 * kStride];
+  uint8_t* ws = stage[threadIdx.x >> 6];
   u32x4_t w[kLoads];
-  if constexpr (!kF32In) {
-    uint32_t b = col0 + lane, r = row0;
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) {
+    const uint32_t c = h * 64 + lane, blk = c / kLoads, chunk = c % kLoads;
+    uint32_t b = col0 + blk, r = row0;
     while (b >= p.nblk_row) { b -= p.nblk_row; ++r; }
-    const u32x4_t* src =
-        reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + (valid ? (int64_t)r * p.ldx + (int64_t)b * 32 : 0));
-#pragma unroll
-    for (int h = 0; h < kLoads; ++h) w[h] = valid ? src[h] : u32x4_t{0, 0, 0, 0};
-  } else {
-    constexpr int kStride = kLoads * 16 + 16;
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads / 64][64 * kStride];
-    uint8_t* ws = stage[threadIdx.x >> 6];
-#pragma unroll
-    for (int h = 0; h < kLoads; ++h) {
-      const uint32_t c = h * 64 + lane, blk = c / kLoads, chunk = c % kLoads;
-      uint32_t b = col0 + blk, r = row0;
-      while (b >= p.nblk_row) { b -= p.nblk_row; ++r; }
-      const bool ok = blk < left;
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
-          static_cast<const float*>(p.x) + (ok ? (int64_t)r * p.ldx + (int64_t)b * 32 + chunk * 4 : 0));
-      w[h] = ok ? __builtin_nontemporal_load(src) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int h = 0; h < kLoads; ++h) {
-      const uint32_t c = h * 64 + lane;
-      *reinterpret_cast<u32x4_t*>(ws + (c / kLoads) * kStride + (c % kLoads) * 16) = w[h];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < kLoads; ++h) w[h] = *reinterpret_cast<const u32x4_t*>(ws + lane * kStride + h * 16);
+    const bool ok = blk < left;
+    const int64_t eo = ok ? (int64_t)r * p.ldx + (int64_t)b * 32 + chunk * (kF32In ? 4 : 8) : 0;
+    const u32x4_t* src = kF32In ? reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + eo)
+                                : reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + eo);
+    w[h] = ok ? __builtin_nontemporal_load(src) : u32x4_t{0, 0, 0, 0};
   }
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) {
+    const uint32_t c = h * 64 + lane;
+    *reinterpret_cast<u32x4_t*>(ws + (c / kLoads) * kStride + (c % kLoads) * 16) = w[h];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) w[h] = *reinterpret_cast<const u32x4_t*>(ws + lane * kStride + h * 16);
 
   double v[32];
 #pragma unroll
