@@ -253,18 +253,39 @@ def test_rotated_layer_every_output(size, M, N, K):
     log(f"   max |dY|/S = {worst:.2e}; relative error vs X W^T: rotated RFQ {err(y):.3e}, plain RFQ {err(y_plain):.3e}")
 
 
-@pytest.mark.parametrize("size", [32, 64])
-def test_rotated_full_size_sampled(size):
-    """The Wan2.2-style layer's full X through the rotated activation pass
-    (the launch the benchmark's rotated line times); sampled rows bit-exact."""
-    cfg = workloads.CONFIGS["wan22_ffn"]
+_FULL_X = {}
+
+
+def full_x(name):
+    """The configuration's full bf16 X (generated once per module)."""
+    if name not in _FULL_X:
+        _FULL_X.clear()
+        _FULL_X[name] = workloads.x_bf16(workloads.CONFIGS[name])
+    return _FULL_X[name]
+
+
+@pytest.mark.parametrize("name,size", [("wan22_ffn", 32), ("wan22_ffn", 64), ("dit_ffn_down", 32), ("dit_ffn_down", 64)])
+def test_rotated_full_size_sampled(name, size):
+    """A configuration's full X through the rotated activation pass (the
+    launches the benchmark's rotated lines time: 4096 x 5120 and
+    32768 x 13824) and its full W through the rotated weight pass; sampled
+    rows bit-exact. The workload's own values, checked against the
+    exactness condition, not adjusted."""
+    cfg = workloads.CONFIGS[name]
     log(f"[rotate] full size {cfg.name}, size {size}")
-    xb = workloads.x_bf16(cfg)
+    xb = full_x(name)
     qx, sx, qr, sr = rfq.rotate_residual_quantize(dev_bf16(xb), size)
+    wb = workloads.w_bf16(cfg)
+    wq, sw = rfq.rotate_quantize_weight(dev_bf16(wb), size)
     torch.cuda.synchronize()
     rows = workloads.sample_rows(cfg, n_random=62)
     x64 = oracle.bf16_bits_to_f64(xb[rows])
-    assert_exactness(x64, size)        # the workload's own values: checked, not adjusted
+    assert_exactness(x64, size)
     want = oracle.rotate_residual_quantize(x64, size)
     got = tuple(t[torch.from_numpy(rows).cuda()] for t in (qx, sx, qr, sr))
-    check_rfq(got, want, "rotated wan22 rows")
+    check_rfq(got, want, f"rotated {name} rows n={size}")
+    wrows = np.unique(np.concatenate([[0, cfg.N - 1], np.random.default_rng(cfg.seed + 7).choice(cfg.N, 62, replace=False)]))
+    w64 = oracle.bf16_bits_to_f64(wb[wrows])
+    assert_exactness(w64, size)
+    gw = tuple(t[torch.from_numpy(wrows).cuda()] for t in (wq, sw))
+    check_mx(gw, oracle.rotate_quantize_weight(w64, size), f"rotated {name} W rows n={size}")
