@@ -25,10 +25,11 @@
 // accumulators per lane either way). K advances
 // 128 elements (64 bytes of codes per row) per stage, as two MFMA steps of
 // 64. When the tile count leaves a last partial round on the CUs, that
-// round's tiles are split, in a second launch, into upper and lower halves
-// (128 x 256 on 8 waves of 32 x 128, one workgroup per CU) or, for the
-// formats whose main tile is already 128 rows, into quadrants (4 waves,
-// two workgroups per CU). The bf16 product of the backward pass's dX also
+// round's tiles are split into upper and lower halves (128 x 256 on 8 waves
+// of 32 x 128, one workgroup per CU; when the whole rounds stream, in the
+// same launch, see gemm_pair_kernel) or, for the formats whose main tile is
+// already 128 rows, into quadrants (4 waves, two workgroups per CU, in a
+// second launch). The bf16 product of the backward pass's dX also
 // has 256 x 320 tiles (8 waves of 64 x 160), used alone when they cover Y
 // in whole rounds and 256 x 256 tiles would not.
 //
@@ -234,14 +235,24 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 1) & 3u; }
 // It must be inlined into the kernel itself: in a called function the
 // segment pointer is not passed along (the compiler substitutes 0), which is
 // why every lambda of the kernel body is marked always_inline.
+// kSlot picks the block: 0 for a one-tile-shape launch, 0 or 1 for the two
+// blocks of a launch that runs two tile shapes (GemmPairParams).
 typedef __attribute__((address_space(4))) const GemmParams* const_params_ptr;
+template <int kSlot>
 __device__ __forceinline__ GemmParams fresh_params() {
-  const_params_ptr q = (const_params_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  const_params_ptr q = (const_params_ptr)__builtin_amdgcn_kernarg_segment_ptr() + kSlot;
   asm volatile("" : "+s"(q));
   GemmParams r;
   __builtin_memcpy(&r, (const GemmParams*)q, sizeof(r));
   return r;
 }
+
+// Two parameter blocks back to back: a launch whose first `a.wg` workgroups
+// run one tile shape and the rest another.
+struct GemmPairParams {
+  GemmParams a, b;
+};
+static_assert(offsetof(GemmPairParams, b) == sizeof(GemmParams), "parameter blocks back to back");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // gfx9 raw buffer: stride 0, num_records in bytes, dword3 = 32-bit data format
@@ -429,8 +440,8 @@ __device__ __forceinline__ void mfma16_group(f32x4_t (&acc)[kT16M][kT16N], const
 // kStream (needs kFast): every tile of the launch lies inside Y and Y takes
 // vector stores, and each workgroup streams several tiles; otherwise each
 // workgroup computes one tile and stores it with per-element bounds checks.
-template <class C, class F, bool kOutBf16, bool kFast, bool kStream>
-__global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParams p) {
+template <class C, class F, bool kOutBf16, bool kFast, bool kStream, int kSlot>
+__device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, uint8_t* const lds) {
   static_assert(kFast || !kStream, "streaming needs whole scale groups");
   constexpr bool kResid = F::kResid;
   constexpr bool kM16 = F::kM16;
@@ -439,11 +450,13 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   constexpr int kWaveM = C::kWaveM, kWaveN = C::kWaveN, kTM = C::kTM, kTN = C::kTN;
   constexpr int kTileBytesA = C::kTileBytesA, kStageBytes = C::kStageBytes;
   constexpr int kScaleBytesA = C::kScaleBytesA;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
   uint8_t* const ring = lds;
   uint8_t* const sbuf = lds + kRing * kStageBytes;
 
-  const unsigned lane = threadIdx.x & 63;
+  // (the lane from mbcnt, not from the thread index: the thread index then
+  // dies once the wave index is in a scalar register, instead of holding a
+  // VGPR through the loop for the epilogue)
+  const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   // wave index as a scalar: everything derived from it (row ranges, which
   // operand a scale piece belongs to) stays in SGPRs and scalar branches
   const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -454,9 +467,9 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // already being fetched, and the finished tile's stores drain behind the
   // next tile's MFMAs. (Streaming needs whole scale groups per tile, kFast;
   // otherwise the launch gives each workgroup one item.)
-  const int ntiles = (p.grid - (int)blockIdx.x + p.wg - 1) / p.wg;
+  const int ntiles = (p.grid - bid + p.wg - 1) / p.wg;
   int cm0, cn0;                                  // origin of the tile being computed
-  tile_origin(p, blockIdx.x, cm0, cn0);
+  tile_origin(p, bid, cm0, cn0);
   if (cm0 >= p.M || cn0 >= p.N) return;          // a quadrant past the edge (whole workgroup)
   const int nstages = (p.K + kBK - 1) / kBK;
   const int ngroups = (nstages + kScaleGroup - 1) / kScaleGroup;
@@ -918,9 +931,9 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       // has been issued, and none of the new one)
       ++load_tile;
       load_base += nstages;
-      const GemmParams q = fresh_params();
+      const GemmParams q = fresh_params<kSlot>();
       int m0, n0;
-      tile_origin(q, (int)blockIdx.x + load_tile * q.wg, m0, n0);
+      tile_origin(q, bid + load_tile * q.wg, m0, n0);
       set_load_tile(q, m0, n0);
     }
     if (P == 2) issue_scales(st / kScaleGroup + 1);
@@ -1058,7 +1071,7 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   // 8 (q / 4) + 4 lhalf + (0..3), stored together (8 bytes of bf16 or 16 of
   // fp32) when the host found Y's base and row stride aligned for it.
   auto store_tile = [&](int em0, int en0) __attribute__((always_inline)) {
-    const GemmParams q = fresh_params();
+    const GemmParams q = fresh_params<kSlot>();
     if constexpr (kM16) {
       // 16 x 16 tiles: lane (lane / 16, lane % 16) has row m of Y and the
       // four consecutive columns 16 n + 4 (lane / 16) + (0..3) of tile n
@@ -1183,12 +1196,16 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       store_tile(em0, en0);
       return;
     }
-    const GemmParams q = fresh_params();
+    const GemmParams q = fresh_params<kSlot>();
     if constexpr (kM16) {
+      // (the lane recomputed here, so that nothing derived from it has to
+      // stay live through the K loop for this epilogue)
+      uint32_t sl = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      asm volatile("" : "+v"(sl));
 #pragma unroll
       for (int i = 0; i < C::kT16M; ++i) {
         const int64_t at =
-            (int64_t)(em0 + (int)a_row0 + (int)(lane & 15) + 16 * i) * q.ldy + en0 + (int)b_row0 + 4 * (int)(lane >> 4);
+            (int64_t)(em0 + (int)a_row0 + (int)(sl & 15) + 16 * i) * q.ldy + en0 + (int)b_row0 + 4 * (int)(sl >> 4);
         uint16_t* yb = reinterpret_cast<uint16_t*>(q.y) + at;
         float* yf = reinterpret_cast<float*>(q.y) + at;
 #pragma unroll
@@ -1254,8 +1271,8 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
       zero_acc();
       ++comp_tile;
       comp_base += nstages;
-      const GemmParams q = fresh_params();
-      tile_origin(q, (int)blockIdx.x + comp_tile * q.wg, cm0, cn0);
+      const GemmParams q = fresh_params<kSlot>();
+      tile_origin(q, bid + comp_tile * q.wg, cm0, cn0);
     }
     const uint32_t r0 = rot[0];
     rot[0] = rot[1];
@@ -1266,6 +1283,27 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
     store_full_tile(cm0, cn0);
   else
     store_tile(cm0, cn0);
+}
+
+template <class C, class F, bool kOutBf16, bool kFast, bool kStream>
+__global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
+  gemm_body<C, F, kOutBf16, kFast, kStream, 0>(p, (int)blockIdx.x, lds);
+}
+
+// The streamed whole rounds of big tiles and the halves of the last partial
+// round in one launch: workgroups 0 .. a.wg - 1 stream big tiles (one per
+// CU), the rest take one half each, so each half starts on a CU as soon as
+// that CU's stream ends (no workgroup waits for another).
+template <class CB, class CH, class F, bool kOutBf16>
+__global__ __launch_bounds__(64 * CB::kWaves, 1) void gemm_pair_kernel(GemmPairParams pp) {
+  static_assert(CB::kWaves == CH::kWaves, "one workgroup size");
+  constexpr int kLds = CB::kLdsBytes > CH::kLdsBytes ? CB::kLdsBytes : CH::kLdsBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  if ((int)blockIdx.x < pp.a.wg)
+    gemm_body<CB, F, kOutBf16, true, true, 0>(pp.a, (int)blockIdx.x, lds);
+  else
+    gemm_body<CH, F, kOutBf16, true, false, 1>(pp.b, (int)blockIdx.x - pp.a.wg, lds);
 }
 
 template <class C, class F, bool kOutBf16, bool kCanStream>
@@ -1290,8 +1328,12 @@ hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipSt
 //    ceil(4 rest / (2 cus)) rounds;
 //  - halves (128 x 256 on 8 waves, one per CU): kHalfRound per
 //    ceil(2 rest / cus) rounds.
-// Quadrants and halves run in a second launch after the whole rounds. The
-// prices are measured: on the 4096 x 13824 x 5120 layer (96 tiles left after
+// Quadrants run in a second launch after the whole rounds, and so do halves
+// when the whole rounds do not stream; behind streamed rounds the halves go
+// in the same launch (gemm_pair_kernel: each CU takes a half as soon as its
+// stream ends, and the gap between two launches goes away; same-box A/B on
+// the 4096 x 5120 x 13824 layer 275.0 against 281.8 us, W4A8 236.8 against
+// 243.3 us; Y bit-identical). The prices are measured: on the 4096 x 13824 x 5120 layer (96 tiles left after
 // three rounds) 384 quadrants took 0.55 of a big round and 192 halves 0.44;
 // on 2048 x 4096 x 4096 (128 tiles, no whole round) one round of halves ran
 // in 0.70 of the big-tile time and of quadrants in 0.84. Halves have the
@@ -1305,7 +1347,7 @@ constexpr double kQuadRound = 0.55, kHalfRound = 0.48;
 constexpr double kQuadRoundBf16 = 0.50, kHalfRoundBf16 = 0.60;
 
 // The launch plan of every variant but in-GEMM quantization (below): big
-// tiles in whole rounds, the rest as halves or quadrants in a second launch.
+// tiles in whole rounds, the rest as halves or quadrants.
 template <class F, bool kOutBf16>
 hipError_t launch_tiled_impl(GemmParams p, bool fast, int cus, int tiles, hipStream_t stream) {
   using Big = typename Tiles<F>::Big;
@@ -1354,6 +1396,19 @@ hipError_t launch_tiled_impl(GemmParams p, bool fast, int cus, int tiles, hipStr
   // workgroup.
   const bool stream_tiles = fast && p.vec_out && p.M % Big::kBM == 0 && p.N % Big::kBN == 0 && big > cus;
   p.wg = stream_tiles ? cus : big;
+  if constexpr (Tiles<F>::kHasHalf && !F::kFusedQ) {
+    if (stream_tiles && tail == kTailHalf && Big::kWaves == Half::kWaves) {
+      GemmPairParams pp;
+      pp.a = p;
+      pp.b = p;
+      pp.b.first = big;
+      pp.b.pieces = 2;
+      pp.b.grid = pp.b.wg = 2 * (tiles - big);
+      hipLaunchKernelGGL((gemm_pair_kernel<Big, Half, F, kOutBf16>), dim3(pp.a.wg + pp.b.wg), dim3(64 * Big::kWaves), 0,
+                         stream, pp);
+      return hipGetLastError();
+    }
+  }
   hipError_t e = launch_tiles<Big, F, kOutBf16, true>(p, fast, stream_tiles, stream);
   if (e != hipSuccess || big == tiles) return e;
   p.first = big;
