@@ -54,6 +54,21 @@ def near_midpoints(rng, rows, K):
     return (v * np.repeat(np.exp2(se), 32, axis=1)).astype(np.float32)
 
 
+def signed_zero_rows(rng, x, r0, zero, neg_zero, one):
+    """Rows r0 and r0 + 1, first 64 columns (one 64-block, two 32-blocks):
+    zeros of random sign, then the same with an equal nonzero pair at every
+    position 4 i + 2, 4 i + 3, so that half of the Hadamard sums cancel
+    exactly amid the signed zeros (every exact zero must come out as +0).
+    Rows or columns past the array's are left out."""
+    n = min(64, x.shape[1])
+    for r in (r0, r0 + 1):
+        if r < x.shape[0]:
+            x[r, :n] = np.where(rng.random(n) < 0.5, neg_zero, zero)
+    if r0 + 1 < x.shape[0]:
+        x[r0 + 1, 2:n:4] = one
+        x[r0 + 1, 3:n:4] = one
+
+
 def heavy_f32(rng, rows, K):
     x = rng.standard_t(3, size=(rows, K)) * np.exp(rng.uniform(-6, 6, size=(rows, 1)))
     x[:, rng.choice(K, size=3, replace=False)] *= 80
@@ -61,15 +76,18 @@ def heavy_f32(rng, rows, K):
     x[0, :32] = 0.0
     x[0, 32:64] = -0.0
     x[1, :16] = np.float32(1e-40)            # float32 subnormals
+    signed_zero_rows(rng, x, 2, np.float32(0.0), np.float32(-0.0), np.float32(1.5))
     return x
 
 
+@pytest.mark.parametrize("rows,K", [(96, 1024), (37, 224)])
 @pytest.mark.parametrize("kind", ["midpoints", "heavy"])
-def test_fp32_input_quantize_and_residual(kind):
-    rng = np.random.default_rng(31 if kind == "midpoints" else 32)
-    rows, K = 96, 1024
+def test_fp32_input_quantize_and_residual(kind, rows, K):
+    """Dense fp32 X: whole waves (96 x 1024) and a ragged last wave
+    (37 x 224, 259 blocks)."""
+    rng = np.random.default_rng((31 if kind == "midpoints" else 32) + rows)
     x = near_midpoints(rng, rows, K) if kind == "midpoints" else heavy_f32(rng, rows, K)
-    log(f"[rotate] fp32 input {kind}")
+    log(f"[rotate] fp32 input {kind} {rows}x{K}")
     xd = dev_f32(x)
     got_q = rfq.quantize_mxfp4(xd)
     got_r = rfq.residual_quantize(xd)
@@ -116,6 +134,7 @@ def spiky_bf16(rng, rows, K):
     bits[3, 40] = 0x7FC0          # NaN
     bits[4, 70] = 0xFF80          # -Inf
     bits[5, :32] = 0x8000         # -0.0 block
+    signed_zero_rows(rng, bits, 6, 0x0000, 0x8000, 0x3FC0)   # 0x3FC0: 1.5
     return bits
 
 
