@@ -286,8 +286,8 @@ def layer_timings(rfq, torch, cfg, x, wq, sw, batch_ms, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by rows of X with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer would shard by rows of X, with no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import torch
