@@ -193,6 +193,7 @@ struct Tiles {
   using Big = TileCfg<256, 256, 8, 1, F>;
   using Quad = TileCfg<128, 128, 4, 2, F>;
   using Half = TileCfg<128, 256, 8, 1, F>;   // upper or lower half of a big tile
+  using Piece = TileCfg<128, 192, 8, 1, F>;  // tiles the last round's rectangle (8 waves of 32 x 96)
   static constexpr bool kHasHalf = true;
 };
 template <class F>
@@ -202,6 +203,7 @@ struct Tiles<F, true> {
   using Big = TileCfg<128, 256, 8, 1, F>;
   using Quad = TileCfg<64, 128, 4, 2, F>;
   using Half = Big;                          // (not used)
+  using Piece = Big;                         // (not used)
   static constexpr bool kHasHalf = false;
 };
 
@@ -220,11 +222,14 @@ struct GemmParams {
   // grid walked in a fixed logical order; item ids map to logical tile
   // first + (0 .. grid - 1), or, split into `pieces` (4: quadrants, 2: upper
   // and lower halves), to piece id % pieces of logical tile first + id /
-  // pieces. The launch has `wg` workgroups; workgroup b runs items b,
-  // b + wg, b + 2 wg, ... back to back.
+  // pieces. With pieces == 3 the items are instead the tiles_m x tiles_n
+  // blocks of gm x gn of the rectangle at (rm0, rn0), item i at block row
+  // i % tiles_m, column i / tiles_m. The launch has `wg` workgroups;
+  // workgroup b runs items b, b + wg, b + 2 wg, ... back to back.
   int32_t tiles_m, tiles_n, gm, gn;
   int32_t first, grid, pieces, wg;
   int32_t vec_out;   // Y base and row stride allow 4-element vector stores
+  int32_t rm0, rn0;
 };
 
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 1) & 3u; }
@@ -299,6 +304,11 @@ __device__ __forceinline__ void tile_origin(const GemmParams& p, int bid, int& m
   const int xcd = bid % 8, idx = bid / 8;
   const int base = total / 8, rem = total % 8;
   const int local = xcd < rem ? xcd * (base + 1) + idx : rem * (base + 1) + (xcd - rem) * base + idx;
+  if (p.pieces == 3) {
+    m0 = p.rm0 + (local % p.tiles_m) * p.gm;
+    n0 = p.rn0 + (local / p.tiles_m) * p.gn;
+    return;
+  }
   const int logical = p.first + local / p.pieces;
   const int q = local % p.pieces;
   const int per_group = kGroupM * p.tiles_n;
@@ -1339,11 +1349,18 @@ hipError_t launch_tiles(const GemmParams& p, bool fast, bool stream_tiles, hipSt
 // in 0.70 of the big-tile time and of quadrants in 0.84. Halves have the
 // 8-wave workgroup's operand reuse (half the fragment reads per MFMA of a
 // 4-wave quadrant) and fill one CU each. The same holds for plain W4A4 and
-// W4A8. The bf16 mode of the backward products is the other way round: its
+// W4A8. Behind streamed rounds, when the last partial round's tiles form a
+// rectangle that 128 x 192 pieces cover in at most one round, the pieces
+// (8 waves of 32 x 96) run there instead of halves. On the 4096 x 5120 x
+// 13824 layer (96 tiles left: a 1024 x 6144 rectangle, 256 pieces on all
+// CUs, where 192 halves leave 64 idle)
+// same-box A/B measured the RFQ GEMM at 275.4 against 276.0 us (equal) and
+// W4A8 at 236.7 against 241.0 us, Y bit-identical; their price is set just
+// below the halves'. The bf16 mode of the backward products is the other way round: its
 // stages are short (32 K elements), and two quadrant workgroups per CU hide
 // each other's barriers better (dX on the 4096 x 5120 x 13824 layer: 554-558
 // us with quadrants, 595-599 us with halves; dW 892-896 against 909-912 us).
-constexpr double kQuadRound = 0.55, kHalfRound = 0.48;
+constexpr double kQuadRound = 0.55, kHalfRound = 0.48, kPieceRound = 0.47;
 constexpr double kQuadRoundBf16 = 0.50, kHalfRoundBf16 = 0.60;
 
 // The launch plan of every variant but in-GEMM quantization (below): big
@@ -1353,6 +1370,7 @@ hipError_t launch_tiled_impl(GemmParams p, bool fast, int cus, int tiles, hipStr
   using Big = typename Tiles<F>::Big;
   using Quad = typename Tiles<F>::Quad;
   using Half = typename Tiles<F>::Half;
+  using Piece = typename Tiles<F>::Piece;
   if constexpr (F::kBf16 && !F::kOutT) {
     // The bf16 product dY Wd: when 256 x 320 tiles (8 waves of 64 x 160)
     // cover Y in whole rounds and 256 x 256 tiles would leave a partial
@@ -1378,12 +1396,12 @@ hipError_t launch_tiled_impl(GemmParams p, bool fast, int cus, int tiles, hipStr
   const int rounds = tiles / cus, rest = tiles % cus;
   enum { kTailBig = 1, kTailQuad = 2, kTailHalf = 3 };
   int tail = kTailBig;
+  double best = 1.0;
   if (rest != 0) {
     const double quad_round = F::kBf16 ? kQuadRoundBf16 : kQuadRound;
     const double half_round = F::kBf16 ? kHalfRoundBf16 : kHalfRound;
     const double t_quad = quad_round * ((4 * rest + 2 * cus - 1) / (2 * cus));
     const double t_half = Tiles<F>::kHasHalf ? half_round * ((2 * rest + cus - 1) / cus) : 1e30;
-    double best = 1.0;
     if (t_quad < best) { best = t_quad; tail = kTailQuad; }
     if (t_half < best) { best = t_half; tail = kTailHalf; }
   }
@@ -1396,6 +1414,39 @@ hipError_t launch_tiled_impl(GemmParams p, bool fast, int cus, int tiles, hipStr
   // workgroup.
   const bool stream_tiles = fast && p.vec_out && p.M % Big::kBM == 0 && p.N % Big::kBN == 0 && big > cus;
   p.wg = stream_tiles ? cus : big;
+  if constexpr (Tiles<F>::kHasHalf && !F::kFusedQ && !F::kBf16) {
+    // The last partial round as one round of 128 x 192 pieces, when its
+    // tiles form a rectangle that such pieces cover exactly: the logical
+    // order walks groups of kGroupM tile rows column by column, so the
+    // leftover tiles are whole columns of the last group when they start at
+    // a column boundary of it.
+    const int per_group = kGroupM * p.tiles_n;
+    const int g_last = big / per_group, g_start = g_last * per_group;
+    const int g_rows = min(p.tiles_m - g_last * kGroupM, kGroupM);
+    const int off = big - g_start;
+    if (stream_tiles && rest != 0 && kPieceRound < best && g_start + g_rows * p.tiles_n == tiles && off % g_rows == 0) {
+      const int tn0 = off / g_rows;
+      const int rows = g_rows * Big::kBM, cols = (p.tiles_n - tn0) * Big::kBN;
+      const int pm = rows / Piece::kBM, pn = cols / Piece::kBN;
+      if (rows % Piece::kBM == 0 && cols % Piece::kBN == 0 && pm * pn <= cus) {
+        GemmPairParams pp;
+        pp.a = p;
+        pp.b = p;
+        pp.b.pieces = 3;
+        pp.b.gm = Piece::kBM;
+        pp.b.gn = Piece::kBN;
+        pp.b.tiles_m = pm;
+        pp.b.tiles_n = pn;
+        pp.b.rm0 = g_last * kGroupM * Big::kBM;
+        pp.b.rn0 = tn0 * Big::kBN;
+        pp.b.first = 0;
+        pp.b.grid = pp.b.wg = pm * pn;
+        hipLaunchKernelGGL((gemm_pair_kernel<Big, Piece, F, kOutBf16>), dim3(pp.a.wg + pp.b.wg),
+                           dim3(64 * Big::kWaves), 0, stream, pp);
+        return hipGetLastError();
+      }
+    }
+  }
   if constexpr (Tiles<F>::kHasHalf && !F::kFusedQ) {
     if (stream_tiles && tail == kTailHalf && Big::kWaves == Half::kWaves) {
       GemmPairParams pp;
@@ -1472,6 +1523,7 @@ hipError_t launch_gemm(int x_fmt, int r_fmt, const uint8_t* qx, const uint8_t* s
   const uintptr_t vec_bytes = y_bf16 ? 8 : 16;
   p.vec_out = (y_trans || ((uintptr_t)y % vec_bytes == 0 && ldy % 4 == 0)) ? 1 : 0;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
+  p.rm0 = p.rn0 = 0;
   const bool fast = (K % (kBK * kScaleGroup)) == 0;
   const int cus = cu_count();
   if (qr == nullptr) r_fmt = 0;
@@ -1506,6 +1558,7 @@ hipError_t launch_gemm_fused(const uint16_t* x, int64_t ldx, const uint8_t* w, c
   const uintptr_t vec_bytes = y_bf16 ? 8 : 16;
   p.vec_out = ((uintptr_t)y % vec_bytes == 0 && ldy % 4 == 0) ? 1 : 0;
   p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
+  p.rm0 = p.rn0 = 0;
   const int cus = cu_count();
   return y_bf16 ? launch_variant<FmtRfqFused, true>(p, true, cus, stream)
                 : launch_variant<FmtRfqFused, false>(p, true, cus, stream);

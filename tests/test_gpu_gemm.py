@@ -269,6 +269,32 @@ def test_streamed_tiles_every_output(M, N, K, out_dtype):
     check_y(y, y_ref, s_ref, out_dtype, f"streamed {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,out_dtype", [(4096, 13824, 512, torch.float32), (1024, 34304, 512, torch.bfloat16)])
+def test_streamed_rounds_then_rectangle_pieces(M, N, K, out_dtype):
+    """Whole streamed rounds, then the last partial round's tiles, which form
+    a rectangle of whole tile columns, as 128 x 192 pieces in the same
+    launch: 4096 x 13824 (the 4096 x 5120 x 13824 layer's tile grid at
+    K = 512) has 864 tiles, three rounds and a 1024 x 6144 rectangle of 256
+    pieces; 1024 x 34304 has 536 tiles, two rounds and a 1024 x 1536
+    rectangle of 64 pieces. Every output of the RFQ GEMM and of the plain
+    W4A4 GEMM on the same operands checked."""
+    rng = np.random.default_rng(M + N + K + 11)
+    xb = heavy(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[gemm] streamed rounds + rectangle pieces M={M} N={N} K={K} {out_dtype}")
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    qx, sx, qr, sr = rfq.residual_quantize(dev_bf16(xb))
+    y = y_host(rfq.gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=out_dtype))
+    y4 = y_host(rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out_dtype=out_dtype))
+    x = oracle.bf16_bits_to_f64(xb)
+    owq, osw = oracle.quantize_mxfp4(oracle.bf16_bits_to_f64(wb))
+    oqx, osx, oqr, osr = oracle.residual_quantize(x)
+    y_ref, s_ref = oracle.gemm_w4a4(oqx, osx, oqr, osr, owq, osw)
+    check_y(y, y_ref, s_ref, out_dtype, f"rectangle pieces RFQ {M}x{N}x{K}")
+    y_ref, s_ref = oracle.gemm_w4a4(oqx, osx, None, None, owq, osw)
+    check_y(y4, y_ref, s_ref, out_dtype, f"rectangle pieces W4A4 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("name", ["qwen3vl_attn_proj", "qwen3vl_ffn_up", "wan22_ffn", "dit_ffn_down"])
 def test_full_size_config(name):
     """The configuration as the benchmark runs it (full X, full W, one
