@@ -225,6 +225,64 @@ def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=No
                     "one 8-wave workgroup per CU (rfq_probe_mfma_ceiling)"}
 
 
+def library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_ms, bdx_ms):
+    """The vendor library's GEMMs on this layer's operands, for context (not
+    part of the path): torch._scaled_mm (hipBLASLt) with MXFP4 operands, as
+    one call on [Q(X) | Q(R)] against [Wq | Wq] (the K-doubled contraction;
+    the concatenations are made outside the timed region) and as the plain
+    W4A4 product, and a bf16 torch.matmul of the dX shape. Unit scales (E8M0
+    code 127) in the MXFP4 calls: the time does not depend on the scale
+    values, and with unit scales every output is a sum of E2M1 products that
+    fp32 holds exactly (|Y| < 36 K, in steps of 1/4): rfq_gemm_w4a4's fp32 Y
+    is that exact sum, and the library's bf16 Y (it takes bf16 or fp16
+    output with block scales) is checked bit for bit against it cut to bf16
+    (the library truncates to bf16 where this GEMM rounds to nearest even),
+    which shows that both read the codes alike."""
+    if not (hasattr(torch, "float4_e2m1fn_x2") and hasattr(torch, "float8_e8m0fnu")):
+        return {"available": False, "reason": "this torch build has no float4_e2m1fn_x2 / float8_e8m0fnu dtypes"}
+    dev = qx.device
+    fp4, e8 = torch.float4_e2m1fn_x2, torch.float8_e8m0fnu
+
+    def unit(rows, k):
+        return torch.full((rows, k // 32), 127, dtype=torch.uint8, device=dev)
+
+    try:
+        ua, ub = unit(M, K), unit(N, K)
+        y_lib = torch._scaled_mm(qx.view(fp4), wq.view(fp4).t(), ua.view(e8), ub.view(e8), out_dtype=torch.bfloat16)
+        y_own = rfq.gemm_w4a4(qx, ua, None, None, wq, ub, out_dtype=torch.float32)
+        cut = (y_own.view(torch.int32) >> 16).to(torch.int16)
+        same = float((y_lib.view(torch.int16) == cut).float().mean())
+        del y_lib, y_own, cut
+        a2, b2 = torch.cat([qx, qr], dim=1), torch.cat([wq, wq], dim=1)
+        ua2, ub2 = unit(M, 2 * K), unit(N, 2 * K)
+        lib_k2_ms = batch_ms(lambda: torch._scaled_mm(a2.view(fp4), b2.view(fp4).t(), ua2.view(e8), ub2.view(e8),
+                                                      out_dtype=torch.bfloat16), 30, warm=5)
+        lib_k_ms = batch_ms(lambda: torch._scaled_mm(qx.view(fp4), wq.view(fp4).t(), ua.view(e8), ub.view(e8),
+                                                     out_dtype=torch.bfloat16), 30, warm=5)
+        del a2, b2, ua2, ub2
+    except Exception as e:   # a torch build without MXFP4 support in _scaled_mm
+        return {"available": False, "reason": f"{type(e).__name__}: {str(e)[:200]}"}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    dy = torch.randn((M, N), generator=gen, device=dev).to(torch.bfloat16)
+    wd = torch.randn((N, K), generator=gen, device=dev).to(torch.bfloat16)
+    mm_ms = batch_ms(lambda: torch.matmul(dy, wd), 10, warm=3)
+    del dy, wd
+    return {
+        "available": True,
+        "what": "torch._scaled_mm (hipBLASLt) with MXFP4 operands and unit scales, bf16 Y; torch.matmul in bf16",
+        "mxfp4_k_doubled_us": round(lib_k2_ms * 1e3, 2),
+        "rfq_gemm_us": round(gemm_ms * 1e3, 2),
+        "rfq_gemm_speedup_over_library": round(lib_k2_ms / gemm_ms, 3),
+        "mxfp4_plain_w4a4_us": round(lib_k_ms * 1e3, 2),
+        "plain_w4a4_us": round(w4a4_ms * 1e3, 2),
+        "plain_w4a4_speedup_over_library": round(lib_k_ms / w4a4_ms, 3),
+        "library_bf16_y_equal_to_exact_y_truncated": round(same, 6),
+        "bf16_matmul_dx_shape_us": round(mm_ms * 1e3, 2),
+        "backward_dx_call_us": round(bdx_ms * 1e3, 2),
+    }
+
+
 def layer_timings(rfq, torch, cfg, x, wq, sw, batch_ms, reps):
     """Quantize pass, GEMM and the whole step (both, back to back) of one
     configuration's layer, each averaged over `reps` back-to-back launches
@@ -468,6 +526,8 @@ def main():
         dy.data_ptr(), 0, M, N, N, qx.data_ptr(), sx.data_ptr(), qr.data_ptr(), sr.data_ptr(), K, g_dw.data_ptr(),
         rfq._lib.DTYPE_BF16, K, ws_dw.data_ptr(), ws_dw.numel(), sp)), 20, warm=10)
     del dy, ws_dx, ws_dw, g_dx, g_dw
+    progress("library reference")
+    library = library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_ms, bdx_ms)
 
     kernel_hash = source_hash("gemm.hip")
     traffic = counter_traffic(args.workload, kernel_hash)
@@ -598,6 +658,7 @@ def main():
                 "rfq_over_w4a4_time": round(gemm_ms / w4a4_ms, 3),
             },
         },
+        "library_reference": library,
     }
     sweep = {}
     progress("configuration sweep")
