@@ -225,12 +225,15 @@ def mfma_ceiling(rfq, torch, qx, qr, wq, stream, sp, iters=2000, reps=5, e4m3=No
                     "one 8-wave workgroup per CU (rfq_probe_mfma_ceiling)"}
 
 
-def library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_ms, bdx_ms):
+def library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_ms, w4a8_ms, bdx_ms):
     """The vendor library's GEMMs on this layer's operands, for context (not
     part of the path): torch._scaled_mm (hipBLASLt) with MXFP4 operands, as
     one call on [Q(X) | Q(R)] against [Wq | Wq] (the K-doubled contraction;
     the concatenations are made outside the timed region) and as the plain
-    W4A4 product, and a bf16 torch.matmul of the dX shape. Unit scales (E8M0
+    W4A4 product; its block-scaled MXFP8 GEMM with both operands in E4M3 (the
+    nearest library operation to W4A8, whose instruction runs at the same
+    rate) and its FP8 GEMM with one scale per tensor; and a bf16 torch.matmul
+    of the dX shape. Unit scales (E8M0
     code 127) in the MXFP4 calls: the time does not depend on the scale
     values, and with unit scales every output is a sum of E2M1 products that
     fp32 holds exactly (|Y| < 36 K, in steps of 1/4): rfq_gemm_w4a4's fp32 Y
@@ -264,13 +267,25 @@ def library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_m
         return {"available": False, "reason": f"{type(e).__name__}: {str(e)[:200]}"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(1)
+    try:
+        a8 = torch.randn((M, K), generator=gen, device=dev).to(torch.float8_e4m3fn)
+        b8 = torch.randn((N, K), generator=gen, device=dev).to(torch.float8_e4m3fn)
+        ua, ub = unit(M, K), unit(N, K)
+        one = torch.ones((), device=dev)
+        mx8_ms = batch_ms(lambda: torch._scaled_mm(a8, b8.t(), ua.view(e8), ub.view(e8), out_dtype=torch.bfloat16),
+                          20, warm=5)
+        fp8_ms = batch_ms(lambda: torch._scaled_mm(a8, b8.t(), one, one, out_dtype=torch.bfloat16), 20, warm=5)
+        del a8, b8
+    except Exception:
+        mx8_ms = fp8_ms = None
     dy = torch.randn((M, N), generator=gen, device=dev).to(torch.bfloat16)
     wd = torch.randn((N, K), generator=gen, device=dev).to(torch.bfloat16)
     mm_ms = batch_ms(lambda: torch.matmul(dy, wd), 10, warm=3)
     del dy, wd
     return {
         "available": True,
-        "what": "torch._scaled_mm (hipBLASLt) with MXFP4 operands and unit scales, bf16 Y; torch.matmul in bf16",
+        "what": "torch._scaled_mm (hipBLASLt) with MXFP4 operands, with E4M3 operands (block scales, or one scale per "
+                "tensor), bf16 Y; torch.matmul in bf16",
         "mxfp4_k_doubled_us": round(lib_k2_ms * 1e3, 2),
         "rfq_gemm_us": round(gemm_ms * 1e3, 2),
         "rfq_gemm_speedup_over_library": round(lib_k2_ms / gemm_ms, 3),
@@ -278,6 +293,9 @@ def library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_m
         "plain_w4a4_us": round(w4a4_ms * 1e3, 2),
         "plain_w4a4_speedup_over_library": round(lib_k_ms / w4a4_ms, 3),
         "library_bf16_y_equal_to_exact_y_truncated": round(same, 6),
+        "mxfp8_e4m3_us": round(mx8_ms * 1e3, 2) if mx8_ms else None,
+        "fp8_per_tensor_scale_us": round(fp8_ms * 1e3, 2) if fp8_ms else None,
+        "w4a8_us": round(w4a8_ms * 1e3, 2),
         "bf16_matmul_dx_shape_us": round(mm_ms * 1e3, 2),
         "backward_dx_call_us": round(bdx_ms * 1e3, 2),
     }
@@ -527,7 +545,7 @@ def main():
         rfq._lib.DTYPE_BF16, K, ws_dw.data_ptr(), ws_dw.numel(), sp)), 20, warm=10)
     del dy, ws_dx, ws_dw, g_dx, g_dw
     progress("library reference")
-    library = library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_ms, bdx_ms)
+    library = library_reference(rfq, torch, qx, qr, wq, M, N, K, batch_ms, gemm_ms, w4a4_ms, w4a8_ms, bdx_ms)
 
     kernel_hash = source_hash("gemm.hip")
     traffic = counter_traffic(args.workload, kernel_hash)
