@@ -26,10 +26,11 @@
 // 128 elements (64 bytes of codes per row) per stage, as two MFMA steps of
 // 64. When the tile count leaves a last partial round on the CUs, that
 // round's tiles are split into upper and lower halves (128 x 256 on 8 waves
-// of 32 x 128, one workgroup per CU; when the whole rounds stream, in the
-// same launch, see gemm_pair_kernel) or, for the formats whose main tile is
-// already 128 rows, into quadrants (4 waves, two workgroups per CU, in a
-// second launch). The bf16 product of the backward pass's dX also
+// of 32 x 128, one workgroup per CU), or, when they form a rectangle that
+// such pieces cover in one round, into 128 x 192 pieces (8 waves of
+// 32 x 96); when the whole rounds stream, either goes in the same launch
+// (see gemm_pair_kernel). Formats whose main tile is already 128 rows split
+// it into quadrants (4 waves, two workgroups per CU, in a second launch). The bf16 product of the backward pass's dX also
 // has 256 x 320 tiles (8 waves of 64 x 160), used alone when they cover Y
 // in whole rounds and 256 x 256 tiles would not.
 //
@@ -184,7 +185,8 @@ struct TileCfg {
 // Main tiles: 256 x 256 outputs, 8 waves of 64 x 128 (128 accumulators
 // each), one workgroup per CU (up to 156 KB of LDS); for the last partial
 // round of a launch, halves of 128 x 256 on 8 waves of 32 x 128, one per
-// CU, or quadrants of 128 x 128 on 4 waves, two per CU. With an E4M3
+// CU, pieces of 128 x 192 on 8 waves of 32 x 96 over the round's
+// rectangle, or quadrants of 128 x 128 on 4 waves, two per CU. With an E4M3
 // residual (three activation sub-tiles) the stage would not fit three deep,
 // so that variant uses 128 x 256 tiles (8 waves of 32 x 128) and 64 x 128
 // quadrants.
@@ -1301,10 +1303,11 @@ __global__ __launch_bounds__(64 * C::kWaves, C::kOcc) void gemm_kernel(GemmParam
   gemm_body<C, F, kOutBf16, kFast, kStream, 0>(p, (int)blockIdx.x, lds);
 }
 
-// The streamed whole rounds of big tiles and the halves of the last partial
-// round in one launch: workgroups 0 .. a.wg - 1 stream big tiles (one per
-// CU), the rest take one half each, so each half starts on a CU as soon as
-// that CU's stream ends (no workgroup waits for another).
+// The streamed whole rounds of big tiles and the last partial round (as
+// halves or rectangle pieces) in one launch: workgroups 0 .. a.wg - 1
+// stream big tiles (one per CU), the rest take one piece each, so each
+// piece starts on a CU as soon as that CU's stream ends (no workgroup waits
+// for another).
 template <class CB, class CH, class F, bool kOutBf16>
 __global__ __launch_bounds__(64 * CB::kWaves, 1) void gemm_pair_kernel(GemmPairParams pp) {
   static_assert(CB::kWaves == CH::kWaves, "one workgroup size");
