@@ -257,11 +257,13 @@ def test_nan_block_gives_nan_outputs_only_in_its_row(variant):
 
 
 @pytest.mark.parametrize("variant,M,N,K", [("w4a8", 4096, 8192, 512), ("fp8_residual", 4096, 4096, 512),
-                                           ("fp8_residual", 2048, 4096, 1024)])
+                                           ("fp8_residual", 2048, 4096, 1024), ("w4a8", 1024, 34304, 512)])
 def test_streamed_tiles_every_output(variant, M, N, K):
     """Two whole rounds of main tiles on 256 CUs (256 x 256 for W4A8, 128 x 256
     for the MXFP8 residual): each workgroup streams its tiles back to back.
-    Every output checked (bf16 Y)."""
+    W4A8 on 1024 x 34304 then runs the last partial round's 1024 x 1536
+    rectangle as 64 pieces of 128 x 192 in the same launch. Every output
+    checked (bf16 Y)."""
     rng = np.random.default_rng(M + N + K + 91)
     xb = heavy_bf16(rng, M, K)
     wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
