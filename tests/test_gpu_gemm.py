@@ -269,6 +269,47 @@ def test_streamed_tiles_every_output(M, N, K, out_dtype):
     check_y(y, y_ref, s_ref, out_dtype, f"streamed {M}x{N}x{K}")
 
 
+def _sweep_shapes():
+    """Seeded random shapes (mostly one partial round, ragged edges, K with
+    and without whole scale groups), then shapes whose tile counts exercise
+    each plan for the last partial round behind streamed rounds: halves
+    (4096 x 10240), and rectangle pieces over a last group of 1, 2 and 3
+    tile rows (1280 x 26368, 3584 x 9472, 1792 x 19712)."""
+    rng = np.random.default_rng(2026)
+    shapes = []
+    for i in range(24):
+        M = int([rng.integers(1, 600), rng.integers(600, 5000), 256 * rng.integers(1, 20)][i % 3])
+        N = int([rng.integers(1, 900), 256 * rng.integers(1, 40), rng.integers(900, 9000)][(i // 3) % 3])
+        K = int(32 * [rng.integers(1, 24), 16 * rng.integers(1, 5)][i % 2])
+        shapes.append((M, N, K))
+    return shapes + [(4096, 10240, 512), (1280, 26368, 512), (3584, 9472, 512), (1792, 19712, 512)]
+
+
+@pytest.mark.parametrize("i,M,N,K", [(i,) + s for i, s in enumerate(_sweep_shapes())])
+def test_shape_sweep_sampled(i, M, N, K):
+    """Every launch plan on sampled outputs: the RFQ layer (fp32 Y on even
+    cases, bf16 Y on odd ones) and plain W4A4, at rows and columns that
+    include the edges and the last 512 rows and 2048 columns (where a last
+    partial round lies)."""
+    rng = np.random.default_rng(5000 + i)
+    out_dtype = torch.float32 if i % 2 == 0 else torch.bfloat16
+    xb = heavy(rng, M, K)
+    wb = workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    log(f"[gemm] sweep {i}: M={M} N={N} K={K} {out_dtype}")
+    x = dev_bf16(xb)
+    wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
+    y = y_host(rfq.linear(x, wq, sw, out_dtype=out_dtype))
+    qx, sx, _, _ = rfq.residual_quantize(x)
+    y4 = y_host(rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out_dtype=out_dtype))
+    pick = lambda n, lo, k: rng.integers(lo, n, size=k) if n > lo else np.zeros(0, np.int64)
+    rows = np.unique(np.concatenate([[0, M - 1, M // 2], rng.integers(0, M, 24), pick(M, max(M - 512, 0), 8)]))
+    cols = np.unique(np.concatenate([[0, N - 1, N // 2], rng.integers(0, N, 40), pick(N, max(N - 2048, 0), 16)]))
+    y_ref, s_ref = oracle_y(xb[rows], wb[cols])
+    check_y(y[np.ix_(rows, cols)], y_ref, s_ref, out_dtype, f"sweep {i} rfq")
+    y_ref, s_ref = oracle_y(xb[rows], wb[cols], resid=False)
+    check_y(y4[np.ix_(rows, cols)], y_ref, s_ref, out_dtype, f"sweep {i} w4a4")
+
+
 @pytest.mark.parametrize("M,N,K,out_dtype", [(4096, 13824, 512, torch.float32), (1024, 34304, 512, torch.bfloat16)])
 def test_streamed_rounds_then_rectangle_pieces(M, N, K, out_dtype):
     """Whole streamed rounds, then the last partial round's tiles, which form
