@@ -109,3 +109,45 @@ def test_empty_input():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     c, s = rfq.quantize_mxfp4(x)
     assert c.shape == (0, 32) and s.shape == (0, 2)
+
+
+def _quantize_sweep():
+    """Seeded (rows, K, row padding, input type) cases: whole and partial
+    last waves (64 blocks per wave), rows shorter than a wave, padded rows."""
+    rng = np.random.default_rng(77)
+    cases = []
+    for i in range(16):
+        rows = int([rng.integers(1, 8), rng.integers(8, 300), rng.integers(300, 3000)][i % 3])
+        K = int(32 * rng.integers(1, 80))
+        pad = int(8 * rng.integers(0, 5)) if i % 4 else 0
+        cases.append((rows, K, pad, "fp32" if i % 2 else "bf16"))
+    return cases
+
+
+@pytest.mark.parametrize("rows,K,pad,dtype", _quantize_sweep())
+def test_quantize_sweep(rows, K, pad, dtype):
+    """Both passes (Q(X) alone, and Q(X) with Q(R)) on dense and padded rows
+    of bf16 and fp32 X, bit-exact against the oracle over the whole tensor."""
+    rng = np.random.default_rng(rows * 31 + K + pad)
+    ldx = K + pad
+    full = (rng.standard_t(3, size=(rows, ldx)) * np.exp(rng.uniform(-8, 8, size=(rows, 1)))).astype(np.float32)
+    log(f"[quantize] sweep rows={rows} K={K} ldx={ldx} {dtype}")
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(full)
+        xd = dev_bf16(bits)[:, :K]
+        x64 = oracle.bf16_bits_to_f64(bits[:, :K])
+    else:
+        xd = torch.from_numpy(full).cuda()[:, :K]
+        x64 = full[:, :K].astype(np.float64)
+    assert xd.stride(0) == ldx
+    c, s = rfq.quantize_mxfp4(xd)
+    qx, sx, qr, sr = rfq.residual_quantize(xd)
+    torch.cuda.synchronize()
+    wc, ws = oracle.quantize_mxfp4(x64)
+    assert_bytes_equal(host(c), oracle.pack_codes(wc), "Q(X) alone codes")
+    assert_bytes_equal(host(s), ws, "Q(X) alone scales")
+    oqx, osx, oqr, osr = oracle.residual_quantize(x64)
+    assert_bytes_equal(host(qx), oracle.pack_codes(oqx), "Q(X) codes")
+    assert_bytes_equal(host(sx), osx, "Q(X) scales")
+    assert_bytes_equal(host(qr), oracle.pack_codes(oqr), "Q(R) codes")
+    assert_bytes_equal(host(sr), osr, "Q(R) scales")
