@@ -4,10 +4,10 @@
 // operand bytes, with no memory traffic inside the loop, timed per workgroup
 // in shader-clock cycles (s_memtime) and in 100 MHz constant-clock ticks
 // (s_memrealtime), so that both the rate and the clock it ran at can be read
-// back. E2M1 x E2M1 runs the 16 x 16 x 128 form the GEMM uses for it (64
-// instructions per wave per iteration over 32 accumulators); E2M1 x E4M3
-// the 32 x 32 x 64 form of the MXFP8 activation variants (32 instructions
-// over 8 accumulators). Both do the same flops per iteration.
+// back. Both operand pairs run the 16 x 16 x 128 form the GEMM uses for
+// them, 64 instructions per wave per iteration over 32 accumulators: E2M1 x
+// E2M1 (RFQ and W4A4) and E2M1 x E4M3 (W4A8), whose instruction takes twice
+// the cycles for the same flops.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -19,7 +19,6 @@ namespace {
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;   // two waves per SIMD, like the GEMM's main tile
 constexpr int kAcc = 8;         // independent accumulators per wave
@@ -41,28 +40,8 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a
   }
   float sum = 0.f;
   uint64_t c0, r0, c1, r1;
-  if constexpr (kBFmt == 8) {
-    f32x16_t acc[kAcc];
-    for (int q = 0; q < kAcc; ++q)
-      for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
-    c0 = __builtin_amdgcn_s_memtime();
-    r0 = __builtin_amdgcn_s_memrealtime();
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int q = 0; q < kAcc; ++q) {
-          const i32x4_t x = ra[(q + s) & 3];
-          acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(i32x8_t{x.x, x.y, x.z, x.w, 0, 0, 0, 0},
-                                                                   rb[(q / 2 + s) & 3], acc[q], 4, 0, 0, 120 + q, 0, 122);
-        }
-    }
-    c1 = __builtin_amdgcn_s_memtime();
-    r1 = __builtin_amdgcn_s_memrealtime();
-    for (int q = 0; q < kAcc; ++q)
-      for (int e = 0; e < 16; ++e) sum += acc[q][e];
-  } else {
-    constexpr int kAcc16 = 4 * kAcc;   // the same accumulator registers as 16 x 16 tiles
+  {
+    constexpr int kAcc16 = 4 * kAcc;   // 32 accumulator tiles of 16 x 16
     f32x4_t acc[kAcc16];
     for (int q = 0; q < kAcc16; ++q)
       for (int e = 0; e < 4; ++e) acc[q][e] = 0.f;
@@ -75,8 +54,8 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(const i32x4_t* a
         for (int q = 0; q < kAcc16; ++q) {
           const i32x4_t x = ra[(q + s) & 3];
           acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(i32x8_t{x.x, x.y, x.z, x.w, 0, 0, 0, 0},
-                                                                    rb[(q / 8 + s) & 3], acc[q], 4, 4, 0, 120 + (q & 7), 0,
-                                                                    122);
+                                                                    rb[(q / 8 + s) & 3], acc[q], 4, kBFmt == 8 ? 0 : 4,
+                                                                    0, 120 + (q & 7), 0, 122);
         }
     }
     c1 = __builtin_amdgcn_s_memtime();

@@ -53,12 +53,12 @@ int rfq_probe_mfma_ceiling(const uint8_t* a_codes, size_t a_bytes, const uint8_t
 
 /*
  * rfq_probe_mfma_ceiling_e4m3 - the same measurement for the instruction of
- * the MXFP8 activation variants, v_mfma_scale_f32_32x32x64_f8f6f4 with the
- * MXFP4 weight first and the E4M3 activation second: 32 MFMAs per wave per
- * iteration over 8 accumulators. Each lane loads eight 16-byte pieces of
- * b_codes (two per operand, 32 bytes) at consecutive positions modulo its
- * size; all else as rfq_probe_mfma_ceiling, including the flop count per
- * call.
+ * the W4A8 GEMM, v_mfma_scale_f32_16x16x128_f8f6f4 with the MXFP4 weight
+ * first and the E4M3 activation second (twice the cycles of the E2M1 x E2M1
+ * form for the same flops): 64 MFMAs per wave per iteration over 32
+ * accumulators. Each lane loads eight 16-byte pieces of b_codes (two per
+ * operand, 32 bytes) at consecutive positions modulo its size; all else as
+ * rfq_probe_mfma_ceiling, including the flop count per call.
  */
 int rfq_probe_mfma_ceiling_e4m3(const uint8_t* a_codes, size_t a_bytes, const uint8_t* b_codes, size_t b_bytes,
                                 int workgroups, int iters, uint64_t* stamps, float* sink, void* stream);

@@ -92,15 +92,22 @@ constexpr int kGroupM = 4;                          // tile rows swept together 
 // weight is E2M1. In LDS a stage row of an E2M1 term is one 64-byte sub-tile
 // (128 elements); an E4M3 term's 128 bytes are two sub-tiles.
 //
-// E4M3 operand layout of the instruction (checked on hardware with one-hot
-// operands and distinct per-lane scales): per row and 64-wide K step, lane
-// half h holds elements 16 h .. 16 h + 15 of K-block 0 in its bytes 0..15 and
-// the same elements of K-block 1 in bytes 16..31; the scale of K-block b is
-// the one supplied by lane half b. (E2M1 operands hold K-block h whole in
-// lane half h.) So the two sub-tiles of an E4M3 term hold, at LDS chunk c =
-// 2 s + lhalf (the chunk an MFMA lane reads in step s), the 16-byte row
-// chunks 4 s + lhalf (first sub-tile) and 4 s + 2 + lhalf (second): row chunk
-// 4 (c / 2) + (c % 2), plus 2 for the second sub-tile.
+// E4M3 operand layouts of the instruction (checked on hardware with one-hot
+// operands and distinct per-lane scales):
+//  * 16 x 16 x 128 form: lane group g (lanes 16 g .. 16 g + 15, row l % 16)
+//    holds elements 16 g .. 16 g + 15 of each 64-wide half of the step, the
+//    first half's in bytes 0..15 and the second's in bytes 16..31, and the
+//    scale of K-block g is the one that lane group supplies (as for E2M1,
+//    whose lane group g holds K-block g whole). So the two sub-tiles of an
+//    E4M3 term are the two 64-byte halves of the stage row, each read like
+//    an E2M1 sub-tile, and the operand is the two fragments side by side.
+//  * 32 x 32 x 64 form: per row and 64-wide K step, lane half h holds
+//    elements 16 h .. 16 h + 15 of K-block 0 in its bytes 0..15 and the same
+//    elements of K-block 1 in bytes 16..31; the scale of K-block b is the
+//    one supplied by lane half b. So the two sub-tiles hold, at LDS chunk
+//    c = 2 s + lhalf (the chunk an MFMA lane reads in step s), the 16-byte
+//    row chunks 4 s + lhalf (first sub-tile) and 4 s + 2 + lhalf (second):
+//    row chunk 4 (c / 2) + (c % 2), plus 2 for the second sub-tile.
 //
 // Format 16 is bfloat16 for every operand (the weight operand too), with no
 // scales: the straight-through backward's products of decoded values. A
@@ -126,9 +133,10 @@ struct Fmts {
   static constexpr int kScalesA = (kBf16 || kQ) ? 0 : (kResid ? 2 : 1);   // activation scale streams (group-wise)
   static constexpr int kScalesB = kBf16 ? 0 : 1;       // weight scale stream
   static constexpr int kTerms = kResid ? 2 : 1;        // MFMAs per output tile per step
-  // E2M1 x E2M1 products run on the 16 x 16 x 128 form of the scaled MFMA
-  // (see the kernel); E4M3 and bf16 operands on the 32 x 32 forms.
-  static constexpr bool kM16 = kX == 4 && (kR == 0 || kR == 4);
+  // E2M1 weights against E2M1 or E4M3 activations (one term) run on the
+  // 16 x 16 x 128 form of the scaled MFMA (see the kernel); an E4M3 residual
+  // term and bf16 operands on the 32 x 32 forms.
+  static constexpr bool kM16 = (kX == 4 && (kR == 0 || kR == 4)) || (kX == 8 && kR == 0);
   static_assert((kX == 4 && (kR == 0 || kR == 4 || kR == 8)) || (kX == 8 && kR == 0) ||
                     (kX == 16 && (kR == 0 || kR == 16)),
                 "formats");
@@ -432,19 +440,25 @@ __device__ __forceinline__ uint32_t gather_stage_bytes(i32x4_t w, uint32_t sel01
 // activation's, which is byte 0 when the GEMM quantizes the activation
 // itself and holds per-stage scale bytes). Terms outermost, so MFMAs into
 // one accumulator are kHM x kHN instructions apart.
-template <int P, int PX, int HW, int HX, int kTerms, int kHM, int kHN, int kT16M, int kT16N>
+template <int P, int PX, int HW, int HX, int kTerms, int kSubA, int kXFmt, int kHM, int kHN, int kT16M, int kT16N>
 __device__ __forceinline__ void mfma16_group(f32x4_t (&acc)[kT16M][kT16N], const i32x4_t (&wf)[2][kHN],
-                                             const i32x4_t (&xf)[2][kHM * kTerms], const uint32_t (&ws)[2][kHN],
+                                             const i32x4_t (&xf)[2][kHM * kSubA], const uint32_t (&ws)[2][kHN],
                                              const uint32_t (&xs)[2][kHM * kTerms]) {
 #pragma unroll
   for (int t = 0; t < kTerms; ++t)
 #pragma unroll
     for (int m = 0; m < kHM; ++m)
 #pragma unroll
-      for (int n = 0; n < kHN; ++n)
+      for (int n = 0; n < kHN; ++n) {
+        // an E4M3 activation (one term, two sub-tiles) is its two fragments
+        // side by side; an E2M1 term is one fragment
+        const i32x4_t& f0 = xf[HX][m * kSubA + (kXFmt == 8 ? 0 : t)];
+        const i32x4_t& f1 = xf[HX][m * kSubA + (kXFmt == 8 ? 1 : t)];
+        const i32x8_t xop = kXFmt == 8 ? i32x8_t{f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w} : widen(f0);
         acc[HX * kHM + m][HW * kHN + n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            widen(wf[HW][n]), widen(xf[HX][m * kTerms + t]), acc[HX * kHM + m][HW * kHN + n], 4, 4, P,
-            (int)ws[HW][n], PX, (int)xs[HX][m * kTerms + t]);
+            widen(wf[HW][n]), xop, acc[HX * kHM + m][HW * kHN + n], 4, kMfmaFmt<kXFmt>, P, (int)ws[HW][n], PX,
+            (int)xs[HX][m * kTerms + t]);
+      }
 }
 
 // kFast: K % 512 == 0 (whole stages and whole 16-block scale groups); the
@@ -505,6 +519,10 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
   // as zero), one per activation sub-tile: an E4M3 term's second sub-tile
   // starts 32 bytes (two chunks) into the row, so the same offsets fetch it.
   const uint32_t kbytes = (uint32_t)p.K / 2, kblocks = (uint32_t)p.K / 32;
+  // where an E4M3 term's second sub-tile starts in a 128-byte stage row: the
+  // second 64-byte half for the 16 x 16 x 128 form, 32 bytes in (two chunks,
+  // interleaved with the first sub-tile's) for the 32 x 32 x 64 form
+  constexpr uint32_t kE4Second = kM16 ? 64u : 32u;
   __amdgpu_buffer_rsrc_t ra[kSubA], rw, rsx, rsr, rsw, rx;
   auto set_load_tile = [&](const GemmParams& q, int m0, int n0) __attribute__((always_inline)) {
     const uint32_t rows_a = (uint32_t)min(kBM, q.M - m0), rows_b = (uint32_t)min(kBN, q.N - n0);
@@ -516,10 +534,16 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
     } else {
       const uint32_t xrow = F::kXFmt == 8 ? 2 * kbytes : kbytes, rrow = F::kRFmt == 8 ? 2 * kbytes : kbytes;
       ra[0] = make_rsrc(q.qx + (int64_t)m0 * xrow, rows_a * xrow);
-      if constexpr (F::kXFmt == 8) ra[1] = make_rsrc(q.qx + (int64_t)m0 * xrow + 32, rows_a * xrow - 32);
+      // (an E4M3 second sub-tile's extent is the tile's bytes past its start,
+      // none when the tile holds fewer: a wrapped extent would let the
+      // out-of-range offset kOOB through)
+      [[maybe_unused]] const uint32_t xbytes = rows_a * xrow, rbytes = rows_a * rrow;
+      if constexpr (F::kXFmt == 8)
+        ra[1] = make_rsrc(q.qx + (int64_t)m0 * xrow + kE4Second, xbytes > kE4Second ? xbytes - kE4Second : 0u);
       if constexpr (F::kResid) {
         ra[F::kXSub] = make_rsrc(q.qr + (int64_t)m0 * rrow, rows_a * rrow);
-        if constexpr (F::kRFmt == 8) ra[F::kXSub + 1] = make_rsrc(q.qr + (int64_t)m0 * rrow + 32, rows_a * rrow - 32);
+        if constexpr (F::kRFmt == 8)
+          ra[F::kXSub + 1] = make_rsrc(q.qr + (int64_t)m0 * rrow + kE4Second, rbytes > kE4Second ? rbytes - kE4Second : 0u);
       }
     }
     rw = make_rsrc(q.w + (int64_t)n0 * kbytes, rows_b * kbytes);
@@ -537,8 +561,10 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
   // Code-tile loads: wave w fetches rows [BM/waves w, BM/waves (w + 1)) of
   // each activation sub-tile and the matching range of W's BN rows, 16 rows
   // per instruction; lane l takes row 16 n + l / 4 of them and LDS chunk
-  // c = (l % 4) ^ f(row), which is row chunk c of an E2M1 sub-tile and row
-  // chunk 4 (c / 2) + c % 2 (+ 2 in the second sub-tile) of an E4M3 term.
+  // c = (l % 4) ^ f(row), which is row chunk c of an E2M1 sub-tile; of an
+  // E4M3 term, row chunk c (+ 4 in the second sub-tile) on the 16 x 16 x 128
+  // form and row chunk 4 (c / 2) + c % 2 (+ 2 in the second) on the
+  // 32 x 32 x 64 form.
   uint32_t lda_chunk[C::kLoadsA], lda_row[C::kLoadsA], ldb_voff[C::kLoadsB], ldb_chunk[C::kLoadsB];
 #pragma unroll
   for (int n = 0; n < C::kLoadsA; ++n) {
@@ -558,7 +584,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
   // byte offset of a lane's chunk in stage 0 of an activation term of format kFmt
   auto lda_voff = [&](auto fmt_c, int n) __attribute__((always_inline)) -> uint32_t {
     constexpr int fmt = decltype(fmt_c)::value;
-    return fmt == 8 ? lda_row[n] * (2 * kbytes) + 64 * (lda_chunk[n] >> 1) + 16 * (lda_chunk[n] & 1)
+    return fmt == 8 ? lda_row[n] * (2 * kbytes) + (kM16 ? 16 * lda_chunk[n] : 64 * (lda_chunk[n] >> 1) + 16 * (lda_chunk[n] & 1))
                     : lda_row[n] * kbytes + 16 * lda_chunk[n];
   };
   constexpr int kDmaPerStage = (F::kFusedQ ? 0 : kSubA * C::kLoadsA) + C::kLoadsB;
@@ -598,8 +624,11 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
         const bool fp8 = is_x ? F::kXFmt == 8 : F::kRFmt == 8;
         const bool second = fp8 && t == (is_x ? 1 : F::kXSub + 1);
         // K-block (within the stage) of this lane's chunk: c for E2M1; for
-        // E4M3 2 (c / 2), + 1 in the second sub-tile
-        const uint32_t blk = fp8 ? 2 * (lda_chunk[n] >> 1) + (second ? 1 : 0) : lda_chunk[n];
+        // E4M3 c / 2, + 2 in the second sub-tile (16 x 16 x 128 form), or
+        // 2 (c / 2), + 1 in the second sub-tile (32 x 32 x 64 form)
+        const uint32_t blk = !fp8 ? lda_chunk[n]
+                             : kM16 ? 2 * (second ? 1 : 0) + (lda_chunk[n] >> 1)
+                                    : 2 * (lda_chunk[n] >> 1) + (second ? 1 : 0);
         const uint32_t base = fp8 ? lda_voff(std::integral_constant<int, 8>{}, n) : lda_voff(std::integral_constant<int, 4>{}, n);
         const uint32_t step = fp8 ? 2 * kRowBytes : kRowBytes;
         uint32_t vo = base, so = kst_s * step;
@@ -785,8 +814,9 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
   // scale group (byte s = stage s) and roll over at its last stage the same
   // way.
   constexpr int kHM = C::kT16M / 2, kHN = C::kT16N / 2;
-  constexpr int kXH = kHM * F::kTerms;          // activation fragments per half
-  i32x4_t wf[2][kHN], xf[2][kXH];
+  constexpr int kXH = kHM * F::kTerms;          // activation scale words per half
+  constexpr int kXF = kHM * kSubA;              // activation fragments per half (two per E4M3 term)
+  i32x4_t wf[2][kHN], xf[2][kXF];
   uint32_t ws[2][kHN], xs[2][kXH];
   // lane offset of a 16-row fragment: row lane % 16, chunk lane / 16
   // (swizzled by the row; fragment bases are multiples of 16 rows)
@@ -808,8 +838,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
 #pragma unroll
     for (int m = 0; m < kHM; ++m)
 #pragma unroll
-      for (int t = 0; t < F::kTerms; ++t)
-        xf[h][m * F::kTerms + t] = read_frag(buf + t * kTileBytesA + (a_row0 + 16 * (h * kHM + m)) * kRowBytes);
+      for (int t = 0; t < kSubA; ++t)
+        xf[h][m * kSubA + t] = read_frag(buf + t * kTileBytesA + (a_row0 + 16 * (h * kHM + m)) * kRowBytes);
   };
   auto read_ws16 = [&](auto h_c) __attribute__((always_inline)) {
     constexpr int h = decltype(h_c)::value;
@@ -1023,7 +1053,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
     constexpr int HW = decltype(hw_c)::value, HX = decltype(hx_c)::value;
     constexpr int kReads = decltype(reads_c)::value, kVmem = decltype(vmem_c)::value;
     constexpr int kG = kHM * kHN * F::kTerms;
-    mfma16_group<P, PX, HW, HX, F::kTerms, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
+    mfma16_group<P, PX, HW, HX, F::kTerms, kSubA, F::kXFmt, kHM, kHN, C::kT16M, C::kT16N>(acc16, wf, xf, ws, xs);
     if constexpr (kReads + kVmem > 0) interleave_hint<kReads, kVmem, kG>();
   };
 
@@ -1045,7 +1075,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
       read_ws16(I1{});
       read_xs16(I1{});
     }
-    group16(pc, I0{}, I0{}, std::integral_constant<int, kHN + kXH + kXsReads + (P == 0 ? kHN + (F::kFusedQ ? 0 : kXH) : 0)>{},
+    group16(pc, I0{}, I0{}, std::integral_constant<int, kHN + kXF + kXsReads + (P == 0 ? kHN + (F::kFusedQ ? 0 : kXH) : 0)>{},
             std::integral_constant<int, kFast ? kDmaPerStage - kPart0 + kLoadsX : 0>{});
     __builtin_amdgcn_sched_barrier(0);
     // (W0, A1)
@@ -1067,7 +1097,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
     read_xs16f(st + 1, I0{});
     if (P == 3) read_xs16(I0{});
     quantize_half(st + 2, I1{});
-    group16(pc, I1{}, I1{}, std::integral_constant<int, kXH + kXsReads + (P == 3 && !F::kFusedQ ? kXH : 0)>{}, I0{});
+    group16(pc, I1{}, I1{}, std::integral_constant<int, kXF + kXsReads + (P == 3 && !F::kFusedQ ? kXH : 0)>{}, I0{});
     __builtin_amdgcn_sched_barrier(0);
   };
   auto run_stage = [&](auto pc, int st) __attribute__((always_inline)) {
