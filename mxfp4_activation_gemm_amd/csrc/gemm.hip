@@ -282,6 +282,16 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t*
 
 __device__ __forceinline__ i32x4_t read_frag(const uint8_t* p) { return *reinterpret_cast<const i32x4_t*>(p); }
 
+// Two fp32 values to bfloat16, packed (a in the low half): gfx950's
+// v_cvt_pk_bf16_f32, which rounds to nearest even under the kernel's default
+// round mode and keeps fp32 denormals (the kernels run with denormals
+// preserved); a NaN stays a NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // FP4 operands use the low 4 of the instruction's 8 operand registers.
 __device__ __forceinline__ i32x8_t widen(i32x4_t v) { return i32x8_t{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
 
@@ -1129,16 +1139,11 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
           const f32x4_t& a = acc16[i][j];
           const float v[4] = {a[0], a[1], a[2], a[3]};
           if (kOutBf16) {
-            uint16_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              uint32_t u = __builtin_bit_cast(uint32_t, v[e]);
-              u = (v[e] != v[e]) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u);
-              h[e] = (uint16_t)(u >> 16);
-            }
+            const uint32_t h01 = bf16_pair(v[0], v[1]), h23 = bf16_pair(v[2], v[3]);
+            const uint16_t h[4] = {(uint16_t)h01, (uint16_t)(h01 >> 16), (uint16_t)h23, (uint16_t)(h23 >> 16)};
             uint16_t* dst = reinterpret_cast<uint16_t*>(q.y) + (int64_t)row * q.ldy + col;
             if (q.vec_out && col + 3 < q.N) {
-              *reinterpret_cast<i32x2_t*>(dst) = i32x2_t{(int)(h[0] | ((uint32_t)h[1] << 16)), (int)(h[2] | ((uint32_t)h[3] << 16))};
+              *reinterpret_cast<i32x2_t*>(dst) = i32x2_t{(int)h01, (int)h23};
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -1178,9 +1183,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
               const float v = acc[i][j][4 * g + e];
               const int64_t at = (int64_t)col * q.ldy + row;
               if (kOutBf16) {
-                const uint32_t u = __builtin_bit_cast(uint32_t, v);
-                reinterpret_cast<uint16_t*>(q.y)[at] =
-                    (uint16_t)(((v != v) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                reinterpret_cast<uint16_t*>(q.y)[at] = (uint16_t)bf16_pair(v, 0.f);
               } else {
                 reinterpret_cast<float*>(q.y)[at] = v;
               }
@@ -1199,16 +1202,11 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
           const int col = col_base + 32 * j + 8 * g;
           const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           if (kOutBf16) {
-            uint16_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              uint32_t u = __builtin_bit_cast(uint32_t, v[e]);
-              u = (v[e] != v[e]) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u);
-              h[e] = (uint16_t)(u >> 16);
-            }
+            const uint32_t h01 = bf16_pair(v[0], v[1]), h23 = bf16_pair(v[2], v[3]);
+            const uint16_t h[4] = {(uint16_t)h01, (uint16_t)(h01 >> 16), (uint16_t)h23, (uint16_t)(h23 >> 16)};
             uint16_t* dst = reinterpret_cast<uint16_t*>(q.y) + (int64_t)row * q.ldy + col;
             if (q.vec_out && col + 3 < q.N) {
-              *reinterpret_cast<i32x2_t*>(dst) = i32x2_t{(int)(h[0] | ((uint32_t)h[1] << 16)), (int)(h[2] | ((uint32_t)h[3] << 16))};
+              *reinterpret_cast<i32x2_t*>(dst) = i32x2_t{(int)h01, (int)h23};
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -1254,14 +1252,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
         for (int j = 0; j < C::kT16N; ++j) {
           const f32x4_t& a = acc16[i][j];
           if (kOutBf16) {
-            uint32_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float v = a[e];
-              const uint32_t u = __builtin_bit_cast(uint32_t, v);
-              h[e] = ((v != v) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-            }
-            *reinterpret_cast<i32x2_t*>(yb + 16 * j) = i32x2_t{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16))};
+            *reinterpret_cast<i32x2_t*>(yb + 16 * j) = i32x2_t{(int)bf16_pair(a[0], a[1]), (int)bf16_pair(a[2], a[3])};
           } else {
             *reinterpret_cast<f32x4_t*>(yf + 16 * j) = f32x4_t{a[0], a[1], a[2], a[3]};
           }
@@ -1281,14 +1272,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, const int bid, ui
         for (int g = 0; g < 4; ++g) {
           const f32x16_t& a = acc[i][j];
           if (kOutBf16) {
-            uint32_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float v = a[4 * g + e];
-              const uint32_t u = __builtin_bit_cast(uint32_t, v);
-              h[e] = ((v != v) ? 0x7FC00000u : u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-            }
-            *reinterpret_cast<i32x2_t*>(yb + 32 * j + 8 * g) = i32x2_t{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16))};
+            *reinterpret_cast<i32x2_t*>(yb + 32 * j + 8 * g) =
+                i32x2_t{(int)bf16_pair(a[4 * g], a[4 * g + 1]), (int)bf16_pair(a[4 * g + 2], a[4 * g + 3])};
           } else {
             *reinterpret_cast<f32x4_t*>(yf + 32 * j + 8 * g) = f32x4_t{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
           }

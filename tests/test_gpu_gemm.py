@@ -336,6 +336,51 @@ def test_streamed_rounds_then_rectangle_pieces(M, N, K, out_dtype):
     check_y(y4, y_ref, s_ref, out_dtype, f"rectangle pieces W4A4 {M}x{N}x{K}")
 
 
+def _rne_bf16_bits(y32):
+    """fp32 to bfloat16 bits by round to nearest even, in integer arithmetic
+    (NaNs are checked separately)."""
+    u = y32.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (4096, 8192, 512), (4096, 13824, 512)])
+def test_bf16_output_is_rne_of_fp32_output(M, N, K):
+    """The bf16 epilogue rounds each fp32 accumulator to nearest even: every
+    bf16 output equals the RNE rounding of the fp32 output of the same GEMM
+    on the same operands, bit for bit, and NaN stays NaN. Three store paths:
+    one partial round of single tiles (300 x 520), streamed whole rounds
+    (4096 x 8192) and streamed rounds followed by rectangle pieces (4096 x
+    13824). Codes are random bytes; each row's E8M0 scales are a base drawn
+    from 0..246 plus 0..7 per block, so that the product of a row pair's
+    scales, which sets the output's magnitude, spans the fp32 denormal
+    range, the normal range and values past the largest finite one (inf);
+    a few blocks carry the NaN scale."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    kb = K // 32
+
+    def scales(rows):
+        return (rng.integers(0, 247, size=(rows, 1)) + rng.integers(0, 8, size=(rows, kb))).astype(np.uint8)
+
+    qx, qr, wq = (dev_u8(rng.integers(0, 256, size=(r, K // 2), dtype=np.uint8)) for r in (M, M, N))
+    sx_h, sr_h, sw_h = scales(M), scales(M), scales(N)
+    sx_h[rng.integers(0, M, 2), rng.integers(0, kb, 2)] = 255
+    sx, sr, sw = dev_u8(sx_h), dev_u8(sr_h), dev_u8(sw_h)
+    log(f"[gemm] bf16 epilogue against RNE of the fp32 output M={M} N={N} K={K}")
+    y32 = host(rfq.gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.float32))
+    y16 = rfq.gemm_w4a4(qx, sx, qr, sr, wq, sw, out_dtype=torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(y32)
+    assert nan.any() and np.isinf(y32).any()
+    tiny = (y32 != 0) & (np.abs(y32) < np.float32(2.0 ** -126))
+    assert tiny.any(), "no fp32 denormal outputs drawn"
+    h_nan = y16[nan]
+    assert ((h_nan & 0x7F80) == 0x7F80).all() and ((h_nan & 0x7F) != 0).all(), "NaN outputs must stay NaN"
+    want = _rne_bf16_bits(y32)
+    bad = np.flatnonzero((y16 != want) & ~nan)
+    assert bad.size == 0, (f"{bad.size} bf16 outputs differ from RNE of fp32, first at {bad[0]}: "
+                           f"fp32 {y32.flat[bad[0]]!r} bf16 {y16.flat[bad[0]]:#06x} want {want.flat[bad[0]]:#06x}")
+    log(f"   {y32.size} outputs: {int(tiny.sum())} denormal, {int(np.isinf(y32).sum())} inf, {int(nan.sum())} NaN")
+
+
 @pytest.mark.parametrize("name", ["qwen3vl_attn_proj", "qwen3vl_ffn_up", "wan22_ffn", "dit_ffn_down"])
 def test_full_size_config(name):
     """The configuration as the benchmark runs it (full X, full W, one
