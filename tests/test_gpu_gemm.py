@@ -393,7 +393,8 @@ def test_full_size_config(name):
       * Y at 128 sampled rows x 256 sampled columns, both as bf16 Y (the
         benchmark's output) and as fp32 Y from a second call, the latter at
         the plain 1e-5 S + 2^-126 gate (with K/128 fp32 accumulations per
-        product: 80 at K = 5120, 216 at K = 13824)."""
+        product: 80 at K = 5120, 216 at K = 13824) and, beyond it, equal to
+        the oracle's exact sum rounded once to fp32 (see below)."""
     import oracle_pool
     cfg = workloads.CONFIGS[name]
     log(f"[gemm] full size {name} M={cfg.M} N={cfg.N} K={cfg.K}: oracle codes on {oracle_pool.workers()} "
@@ -427,7 +428,22 @@ def test_full_size_config(name):
         y_ref, s_ref = oracle_y(xb[rows], wb[cols])
         worst = check_y(yh, y_ref, s_ref, torch.bfloat16, f"{name} bf16 Y")
         worst32 = check_y(y32h, y_ref, s_ref, torch.float32, f"{name} fp32 Y")
-        log(f"   Y ok: max |dY|/S = {worst:.2e} (bf16 Y), {worst32:.2e} (fp32 Y)")
+        # Every term of an output is a multiple of 2^(se_a + se_w - 256) for
+        # its block's E8M0 codes (E2M1 magnitudes are multiples of 1/2), so
+        # where S < 2^24 times the smallest such unit over the output's
+        # blocks every partial sum is exact in fp32, whatever the order of
+        # additions, and fp32 Y must be the exact sum rounded once to fp32.
+        _, osx_s, _, osr_s = oracle.residual_quantize(oracle.bf16_bits_to_f64(xb[rows]))
+        unit_e = np.minimum(np.min(osx_s.astype(np.int32)[:, None, :] + osw.astype(np.int32)[None, :, :], axis=2),
+                            np.min(osr_s.astype(np.int32)[:, None, :] + osw.astype(np.int32)[None, :, :], axis=2)) - 256
+        covered = s_ref < np.ldexp(1.0, unit_e + 24)
+        exact = y32h == y_ref.astype(np.float32).astype(np.float64)
+        log(f"   Y ok: max |dY|/S = {worst:.2e} (bf16 Y), {worst32:.2e} (fp32 Y); the exactness condition holds "
+            f"at {100 * covered.mean():.2f}% of the sampled outputs, fp32 Y equals the exact sum rounded once "
+            f"to fp32 at {100 * exact.mean():.2f}%")
+        assert covered.any(), f"{name}: the exactness condition holds at no sampled output"
+        assert exact[covered].all(), (f"{name}: {int((covered & ~exact).sum())} sampled fp32 outputs whose sums are "
+                                      f"exact in fp32 differ from the exact sum rounded to fp32")
         del xb, wb
         log("   waiting for the oracle's codes of all rows")
         oqx, osx, oqr, osr = codes_job.result(timeout=600)
