@@ -114,6 +114,49 @@ def check_y(y_gpu, y_ref, s_ref, out_dtype, what="", extra=None):
     return worst
 
 
+def exact_cover(s_ref, pairs, chunk=64):
+    """Outputs of an E2M1 x E2M1 contraction whose fp32 accumulation is exact
+    in any order of additions. A term of output (r, c) in K-block b is a
+    multiple of 2^(sa[r, b] + sw[c, b] - 256) (E2M1 magnitudes are multiples
+    of 1/2, E8M0 code e is 2^(e - 127)); where S is below 2^24 times the
+    smallest such unit over the output's blocks and products, and that unit
+    is not below fp32's smallest denormal 2^-149, every partial sum is a
+    multiple of the unit below 2^24 of it, so exact in fp32, and so is Y.
+    pairs: [(sa [rows, K/32], sw [cols, K/32]), ...], the E8M0 codes of each
+    product's operands. Returns a boolean [rows, cols] mask."""
+    rows, cols = s_ref.shape
+    unit = np.full((rows, cols), 1 << 20, np.int64)
+    for sa, sw in pairs:
+        sa, sw = np.asarray(sa, np.int32), np.asarray(sw, np.int32)
+        for r0 in range(0, rows, chunk):
+            m = np.min(sa[r0:r0 + chunk, None, :] + sw[None, :, :], axis=2)
+            unit[r0:r0 + chunk] = np.minimum(unit[r0:r0 + chunk], m)
+    unit -= 256
+    with np.errstate(invalid="ignore"):
+        return (s_ref < np.ldexp(1.0, unit + 24)) & (unit >= -149)
+
+
+def rne_bf16(v):
+    """float64 values exactly representable in fp32, rounded to bfloat16 by
+    round to nearest even (integer arithmetic on the fp32 bits)."""
+    u = np.asarray(v, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    h = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
+    return (h << 16).view(np.float32).astype(np.float64)
+
+
+def check_exact_where_covered(y_gpu, y_ref, s_ref, pairs, out_dtype, what=""):
+    """Where exact_cover holds, Y must be the exact sum itself (fp32 Y) or
+    its round-to-nearest-even to bfloat16 (bf16 Y), bit for bit. Returns the
+    covered fraction."""
+    cov = exact_cover(s_ref, pairs)
+    y_gpu = np.asarray(y_gpu, np.float64)
+    want = y_ref if out_dtype != torch.bfloat16 else rne_bf16(y_ref)
+    bad = np.argwhere(cov & ~(y_gpu == want))
+    assert bad.size == 0, (f"{what}: {len(bad)} outputs whose sums are exact in fp32 differ from the exact sum"
+                           f"{' rounded to bf16' if out_dtype == torch.bfloat16 else ''}, first {bad[:3].tolist()}")
+    return float(cov.mean())
+
+
 def check_grad(g_gpu, g_ref, s_ref, contraction, out_dtype, what=""):
     """Per-output check of a straight-through gradient computed with bf16
     matrix instructions: products of bf16 dY and decoded MXFP4 values are

@@ -1,6 +1,8 @@
 """GPU parity of the W4A4 GEMM and the whole RFQ linear layer against the
 oracle: codes and scales bit-exact, Y within 1e-5 of the condition scale
-per output (plus the bf16 rounding half-ulp for bf16 outputs)."""
+per output (plus the bf16 rounding half-ulp for bf16 outputs), and, at every
+output whose sum the arithmetic makes exact in fp32 (gpu_helpers.exact_cover),
+Y bit-equal to the exact sum (fp32) or to its RNE to bf16."""
 import numpy as np
 import pytest
 import torch
@@ -8,8 +10,8 @@ import torch
 import mxfp4_activation_gemm_amd as rfq
 import oracle
 import workloads
-from gpu_helpers import (REL_TOL, assert_bytes_equal, check_y, dev_bf16, dev_u8, host, host_bf16_as_f64, log,
-                         oracle_mx, oracle_rfq)
+from gpu_helpers import (REL_TOL, assert_bytes_equal, check_exact_where_covered, check_y, dev_bf16, dev_u8, host,
+                         host_bf16_as_f64, log, oracle_mx, oracle_rfq)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,14 +28,19 @@ def y_host(y):
     return host_bf16_as_f64(y) if y.dtype == torch.bfloat16 else host(y).astype(np.float64)
 
 
-def oracle_y(x_bits, w_bits, resid=True):
+def oracle_y(x_bits, w_bits, resid=True, with_scales=False):
+    """Oracle Y and S; with_scales adds the E8M0 codes of each product's
+    operands, [(sx, sw), (sr, sw)] (the residual pair only with resid)."""
     x = oracle.bf16_bits_to_f64(x_bits)
     w = oracle.bf16_bits_to_f64(w_bits)
     wq, sw = oracle.quantize_mxfp4(w)
     qx, sx, qr, sr = oracle.residual_quantize(x)
     if not resid:
         qr = sr = None
-    return oracle.gemm_w4a4(qx, sx, qr, sr, wq, sw)
+    y, s = oracle.gemm_w4a4(qx, sx, qr, sr, wq, sw)
+    if with_scales:
+        return y, s, [(sx, sw)] + ([(sr, sw)] if resid else [])
+    return y, s
 
 
 def heavy(rng, rows, K, outliers=3):
@@ -64,13 +71,16 @@ def test_ragged_shapes_every_output(M, N, K, out_dtype):
     x = dev_bf16(xb)
     wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
     y = rfq.linear(x, wq, sw, out_dtype=out_dtype)
-    y_ref, s_ref = oracle_y(xb, wb)
+    y_ref, s_ref, pairs = oracle_y(xb, wb, with_scales=True)
     check_y(y_host(y), y_ref, s_ref, out_dtype, f"rfq {M}x{N}x{K}")
+    cov = check_exact_where_covered(y_host(y), y_ref, s_ref, pairs, out_dtype, f"rfq {M}x{N}x{K}")
     # plain W4A4 through the same kernel family
     qx, sx, _, _ = rfq.residual_quantize(x)
     y1 = rfq.gemm_w4a4(qx, sx, None, None, wq, sw, out_dtype=out_dtype)
-    y1_ref, s1_ref = oracle_y(xb, wb, resid=False)
+    y1_ref, s1_ref, pairs1 = oracle_y(xb, wb, resid=False, with_scales=True)
     check_y(y_host(y1), y1_ref, s1_ref, out_dtype, f"w4a4 {M}x{N}x{K}")
+    cov1 = check_exact_where_covered(y_host(y1), y1_ref, s1_ref, pairs1, out_dtype, f"w4a4 {M}x{N}x{K}")
+    log(f"   exact sums (Y bit-equal to the exact result) at {100 * cov:.1f}% (RFQ), {100 * cov1:.1f}% (W4A4)")
 
 
 def test_all_code_pairs_single_block():
@@ -265,8 +275,10 @@ def test_streamed_tiles_every_output(M, N, K, out_dtype):
     log(f"[gemm] streamed tiles M={M} N={N} K={K} {out_dtype}")
     wq, sw = rfq.quantize_mxfp4(dev_bf16(wb))
     y = y_host(rfq.linear(dev_bf16(xb), wq, sw, out_dtype=out_dtype))
-    y_ref, s_ref = oracle_y(xb, wb)
+    y_ref, s_ref, pairs = oracle_y(xb, wb, with_scales=True)
     check_y(y, y_ref, s_ref, out_dtype, f"streamed {M}x{N}x{K}")
+    cov = check_exact_where_covered(y, y_ref, s_ref, pairs, out_dtype, f"streamed {M}x{N}x{K}")
+    log(f"   exact sums at {100 * cov:.1f}% of the outputs, each bit-equal to the exact result")
 
 
 def _sweep_shapes():
@@ -304,10 +316,12 @@ def test_shape_sweep_sampled(i, M, N, K):
     pick = lambda n, lo, k: rng.integers(lo, n, size=k) if n > lo else np.zeros(0, np.int64)
     rows = np.unique(np.concatenate([[0, M - 1, M // 2], rng.integers(0, M, 24), pick(M, max(M - 512, 0), 8)]))
     cols = np.unique(np.concatenate([[0, N - 1, N // 2], rng.integers(0, N, 40), pick(N, max(N - 2048, 0), 16)]))
-    y_ref, s_ref = oracle_y(xb[rows], wb[cols])
+    y_ref, s_ref, pairs = oracle_y(xb[rows], wb[cols], with_scales=True)
     check_y(y[np.ix_(rows, cols)], y_ref, s_ref, out_dtype, f"sweep {i} rfq")
-    y_ref, s_ref = oracle_y(xb[rows], wb[cols], resid=False)
+    check_exact_where_covered(y[np.ix_(rows, cols)], y_ref, s_ref, pairs, out_dtype, f"sweep {i} rfq")
+    y_ref, s_ref, pairs = oracle_y(xb[rows], wb[cols], resid=False, with_scales=True)
     check_y(y4[np.ix_(rows, cols)], y_ref, s_ref, out_dtype, f"sweep {i} w4a4")
+    check_exact_where_covered(y4[np.ix_(rows, cols)], y_ref, s_ref, pairs, out_dtype, f"sweep {i} w4a4")
 
 
 @pytest.mark.parametrize("M,N,K,out_dtype", [(4096, 13824, 512, torch.float32), (1024, 34304, 512, torch.bfloat16)])
@@ -332,8 +346,10 @@ def test_streamed_rounds_then_rectangle_pieces(M, N, K, out_dtype):
     oqx, osx, oqr, osr = oracle.residual_quantize(x)
     y_ref, s_ref = oracle.gemm_w4a4(oqx, osx, oqr, osr, owq, osw)
     check_y(y, y_ref, s_ref, out_dtype, f"rectangle pieces RFQ {M}x{N}x{K}")
+    check_exact_where_covered(y, y_ref, s_ref, [(osx, osw), (osr, osw)], out_dtype, f"rectangle pieces RFQ {M}x{N}x{K}")
     y_ref, s_ref = oracle.gemm_w4a4(oqx, osx, None, None, owq, osw)
     check_y(y4, y_ref, s_ref, out_dtype, f"rectangle pieces W4A4 {M}x{N}x{K}")
+    check_exact_where_covered(y4, y_ref, s_ref, [(osx, osw)], out_dtype, f"rectangle pieces W4A4 {M}x{N}x{K}")
 
 
 def _rne_bf16_bits(y32):
@@ -428,22 +444,15 @@ def test_full_size_config(name):
         y_ref, s_ref = oracle_y(xb[rows], wb[cols])
         worst = check_y(yh, y_ref, s_ref, torch.bfloat16, f"{name} bf16 Y")
         worst32 = check_y(y32h, y_ref, s_ref, torch.float32, f"{name} fp32 Y")
-        # Every term of an output is a multiple of 2^(se_a + se_w - 256) for
-        # its block's E8M0 codes (E2M1 magnitudes are multiples of 1/2), so
-        # where S < 2^24 times the smallest such unit over the output's
-        # blocks every partial sum is exact in fp32, whatever the order of
-        # additions, and fp32 Y must be the exact sum rounded once to fp32.
+        # where every partial sum is exact in fp32 (exact_cover), Y must be
+        # the exact sum itself (fp32) or its RNE to bf16, bit for bit
         _, osx_s, _, osr_s = oracle.residual_quantize(oracle.bf16_bits_to_f64(xb[rows]))
-        unit_e = np.minimum(np.min(osx_s.astype(np.int32)[:, None, :] + osw.astype(np.int32)[None, :, :], axis=2),
-                            np.min(osr_s.astype(np.int32)[:, None, :] + osw.astype(np.int32)[None, :, :], axis=2)) - 256
-        covered = s_ref < np.ldexp(1.0, unit_e + 24)
-        exact = y32h == y_ref.astype(np.float32).astype(np.float64)
-        log(f"   Y ok: max |dY|/S = {worst:.2e} (bf16 Y), {worst32:.2e} (fp32 Y); the exactness condition holds "
-            f"at {100 * covered.mean():.2f}% of the sampled outputs, fp32 Y equals the exact sum rounded once "
-            f"to fp32 at {100 * exact.mean():.2f}%")
-        assert covered.any(), f"{name}: the exactness condition holds at no sampled output"
-        assert exact[covered].all(), (f"{name}: {int((covered & ~exact).sum())} sampled fp32 outputs whose sums are "
-                                      f"exact in fp32 differ from the exact sum rounded to fp32")
+        pairs = [(osx_s, osw), (osr_s, osw)]
+        cov = check_exact_where_covered(y32h, y_ref, s_ref, pairs, torch.float32, f"{name} fp32 Y")
+        check_exact_where_covered(yh, y_ref, s_ref, pairs, torch.bfloat16, f"{name} bf16 Y")
+        log(f"   Y ok: max |dY|/S = {worst:.2e} (bf16 Y), {worst32:.2e} (fp32 Y); sums exact in fp32 at "
+            f"{100 * cov:.2f}% of the sampled outputs, where fp32 Y is the exact sum and bf16 Y its RNE, bit for bit")
+        assert cov > 0.99, f"{name}: sums exact in fp32 at only {100 * cov:.2f}% of the sampled outputs"
         del xb, wb
         log("   waiting for the oracle's codes of all rows")
         oqx, osx, oqr, osr = codes_job.result(timeout=600)
