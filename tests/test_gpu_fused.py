@@ -11,7 +11,7 @@ import torch
 import mxfp4_activation_gemm_amd as rfq
 import oracle
 import workloads
-from gpu_helpers import check_y, dev_bf16, host, host_bf16_as_f64, log
+from gpu_helpers import check_exact_where_covered, check_y, dev_bf16, host, host_bf16_as_f64, log
 
 pytestmark = pytest.mark.gpu
 
@@ -39,9 +39,11 @@ def operands(M, N, K, seed, outliers=3):
             workloads.f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32)))
 
 
-def oracle_y(xb, wb):
-    y, s, _, _ = oracle.linear(oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb))
-    return y, s
+def oracle_y(xb, wb, with_scales=False):
+    """Oracle Y and S; with_scales adds the E8M0 codes of each product's
+    operands, [(sx, sw), (sr, sw)]."""
+    y, s, (_, sx, _, sr), (_, sw) = oracle.linear(oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb))
+    return (y, s, [(sx, sw), (sr, sw)]) if with_scales else (y, s)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 512), (33, 65, 512), (128, 256, 512), (300, 520, 1024), (257, 255, 1536),
@@ -55,8 +57,9 @@ def test_fused_every_output(M, N, K, out_dtype):
     y = rfq.linear_fused(x, wq, sw, out_dtype=out_dtype)
     y2 = rfq.linear(x, wq, sw, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    y_ref, s_ref = oracle_y(xb, wb)
+    y_ref, s_ref, pairs = oracle_y(xb, wb, with_scales=True)
     worst = check_y(y_host(y), y_ref, s_ref, out_dtype, f"fused {M}x{N}x{K}")
+    check_exact_where_covered(y_host(y), y_ref, s_ref, pairs, out_dtype, f"fused {M}x{N}x{K}")
     assert np.array_equal(bits(y), bits(y2)), "fused Y differs from rfq_linear's"
     log(f"   ok, max |dY|/S = {worst:.2e}, bit-equal to rfq_linear")
 
@@ -74,8 +77,9 @@ def test_fused_streamed_tiles_every_output(M, N, K):
     y2 = rfq.linear(x, wq, sw, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert np.array_equal(bits(y), bits(y2)), "fused Y differs from rfq_linear's"
-    y_ref, s_ref = oracle_y(xb, wb)
+    y_ref, s_ref, pairs = oracle_y(xb, wb, with_scales=True)
     worst = check_y(y_host(y), y_ref, s_ref, torch.float32, f"fused streamed {M}x{N}x{K}")
+    check_exact_where_covered(y_host(y), y_ref, s_ref, pairs, torch.float32, f"fused streamed {M}x{N}x{K}")
     log(f"   ok, max |dY|/S = {worst:.2e}")
 
 
